@@ -13,10 +13,15 @@ Readings taken where the pages are silent:
   optimum for N(0,1)).
 * Fit procedure: fold the samples to |z|, fit L/2 positive levels and mirror
   them, so the table is exactly symmetric.  Levels start at the empirical
-  quantiles (i + 1/2)/(L/2) of |z|.  Each iteration puts the cell boundaries
-  at the midpoints of adjacent levels (the first cell starts at 0; a sample
-  on a boundary goes to the upper cell) and moves every level to the mean of
-  its cell; an empty cell keeps its level.
+  quantiles p_i = (i + 1/2)/(L/2) of |z|: with the sorted values x_(0..n-1),
+  h = (n-1)*p_i, j = floor(h), level = x_(j) + (h-j)*(x_(j+1) - x_(j)).
+  Each iteration puts the cell boundaries at the midpoints of adjacent levels
+  (the first cell starts at 0; a sample on a boundary goes to the upper cell)
+  and moves every level to the mean of its cell; an empty cell keeps its level.
+* Summation order of a cell's sum (fixed so that a device fit can match it
+  bit for bit): the samples, in their given order, are cut into blocks of
+  512; each block is summed left to right, then the block sums are added
+  left to right.
 * The table shipped to the kernels is each fitted level rounded (half-even)
   to the nearest bfloat16-representable value, held as fp32.
 * Ternary c is the three-level Lloyd-Max optimum for N(0,1): the fixed point
@@ -32,7 +37,29 @@ from .fp import bf16_rne
 
 SAMPLE_COUNT = 400_000
 ITERATIONS = 200
+SUM_BLOCK = 512
 CODEBOOK_LEVELS = {2: 4, 3: 8, 4: 16}      # bits -> number of levels
+
+
+def ordered_sum(v: np.ndarray, block: int = SUM_BLOCK) -> float:
+    """Sum in the fixed order: blocks of ``block`` left to right, then blocks."""
+    v = np.asarray(v, dtype=np.float64)
+    nb = -(-v.size // block)
+    padded = np.zeros(nb * block)
+    padded[: v.size] = v                       # adding +0.0 changes no sum
+    partial = np.cumsum(padded.reshape(nb, block), axis=1)[:, -1]
+    return float(np.cumsum(partial)[-1])
+
+
+def quantile_init(a_sorted: np.ndarray, half: int) -> np.ndarray:
+    """Empirical quantiles (i + 1/2)/half by linear interpolation of order stats."""
+    n = a_sorted.size
+    p = (np.arange(half, dtype=np.float64) + 0.5) / half
+    h = (n - 1) * p
+    j = np.floor(h).astype(np.int64)
+    t = h - j
+    j1 = np.minimum(j + 1, n - 1)
+    return a_sorted[j] + t * (a_sorted[j1] - a_sorted[j])
 
 
 def lloyd_max_fit(samples: np.ndarray, levels: int, iters: int = ITERATIONS) -> np.ndarray:
@@ -41,14 +68,20 @@ def lloyd_max_fit(samples: np.ndarray, levels: int, iters: int = ITERATIONS) -> 
         raise ValueError("sample fit takes an even number of levels")
     a = np.abs(np.asarray(samples, dtype=np.float64))
     half = levels // 2
-    pos = np.quantile(a, (np.arange(half) + 0.5) / half)
+    pos = quantile_init(np.sort(a), half)
+    nb = -(-a.size // SUM_BLOCK)
+    members = np.zeros((half, nb * SUM_BLOCK))   # row c holds a where cell == c, else +0.0
+    cols = np.arange(a.size)
     for _ in range(iters):
         bounds = 0.5 * (pos[:-1] + pos[1:])
         cell = np.searchsorted(bounds, a, side="right")
-        sums = np.bincount(cell, weights=a, minlength=half)
         counts = np.bincount(cell, minlength=half)
-        nonempty = counts > 0
-        pos = np.where(nonempty, sums / np.maximum(counts, 1), pos)
+        members.fill(0.0)
+        members[cell, cols] = a
+        # same order as ordered_sum(): each block left to right, then the blocks
+        partial = np.cumsum(members.reshape(half, nb, SUM_BLOCK), axis=2)[:, :, -1]
+        sums = np.cumsum(partial, axis=1)[:, -1]
+        pos = np.where(counts > 0, sums / np.maximum(counts, 1), pos)
     return np.concatenate([-pos[::-1], pos])
 
 

@@ -63,7 +63,14 @@ def gaussian400k():
 
 
 @pytest.fixture(scope="session")
-def codebooks(gaussian400k):
-    """Shipped cb2/cb3/cb4 tables from the oracle's fit (seed 0, 400k, 200 it)."""
+def raw_fits(gaussian400k):
+    """Unrounded oracle Lloyd-Max fits keyed by bits (seed 0, 400k, 200 it)."""
     from oracle import codebook
-    return codebook.fit_codebooks(gaussian400k)
+    return {b: codebook.lloyd_max_fit(gaussian400k, n) for b, n in codebook.CODEBOOK_LEVELS.items()}
+
+
+@pytest.fixture(scope="session")
+def codebooks(raw_fits):
+    """Shipped cb2/cb3/cb4 tables (bf16-rounded oracle fits)."""
+    from oracle import codebook
+    return {b: codebook.shipped_table(r) for b, r in raw_fits.items()}

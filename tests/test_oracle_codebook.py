@@ -64,9 +64,9 @@ def test_ternary_c_is_three_level_optimum():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_sample_fit_invariants(gaussian400k, bits):
+def test_sample_fit_invariants(gaussian400k, raw_fits, bits):
     levels = cb.CODEBOOK_LEVELS[bits]
-    raw = cb.lloyd_max_fit(gaussian400k, levels)
+    raw = raw_fits[bits]
     assert np.array_equal(raw, -raw[::-1])          # exact symmetry
     assert np.all(np.diff(raw) > 0)                 # strictly increasing
     # centroid condition on the samples themselves (after 200 iterations)
@@ -86,12 +86,45 @@ def test_sample_fit_two_levels_is_mean_abs(gaussian400k):
 
 
 @pytest.mark.slow
-def test_shipped_tables_are_bf16_and_close(codebooks, gaussian400k):
+def test_shipped_tables_are_bf16_and_close(codebooks, raw_fits):
     for bits, table in codebooks.items():
         assert table.dtype == np.float32
         assert table.shape == (cb.CODEBOOK_LEVELS[bits],)
         low16 = table.view(np.uint32) & 0xFFFF
         assert np.all(low16 == 0)                   # bf16-representable
-        raw = cb.lloyd_max_fit(gaussian400k, cb.CODEBOOK_LEVELS[bits])
+        raw = raw_fits[bits]
         assert np.all(np.abs(table - raw) <= 2.0 ** -8 * np.abs(raw))   # unit roundoff of an 8-bit significand
         assert np.array_equal(table, -table[::-1])
+
+
+def test_fixed_summation_order_matches_scalar_definition(gaussian400k):
+    """The vectorized fit adds in the documented order (blocks of 512, then blocks)."""
+    z = gaussian400k[:5000]
+    a = np.abs(z)
+    half = 4
+    pos = cb.quantile_init(np.sort(a), half)
+    for _ in range(3):
+        bounds = 0.5 * (pos[:-1] + pos[1:])
+        cell = np.searchsorted(bounds, a, side="right")
+        cnt = np.bincount(cell, minlength=half)
+        sums = []                                   # scalar loops in the stated order
+        for c in range(half):
+            tot = 0.0
+            for b0 in range(0, a.size, cb.SUM_BLOCK):
+                part = 0.0
+                for i in range(b0, min(b0 + cb.SUM_BLOCK, a.size)):
+                    if cell[i] == c:
+                        part += float(a[i])
+                tot += part
+            sums.append(tot)
+        pos = np.where(cnt > 0, np.array(sums) / np.maximum(cnt, 1), pos)
+    assert np.array_equal(cb.lloyd_max_fit(z, 8, iters=3)[half:], pos)
+
+
+def test_quantile_init_is_interpolated_order_statistic():
+    a = np.sort(np.array([0.5, 0.1, 0.9, 0.3, 0.7]))
+    # n = 5, p = 0.25 and 0.75 -> h = 1.0 and 3.0: exact order statistics
+    assert np.array_equal(cb.quantile_init(a, 2), np.array([0.3, 0.7]))
+    # numpy's default 'linear' quantile agrees away from its lerp special case
+    r = np.random.default_rng(0).random(1001)
+    assert np.allclose(cb.quantile_init(np.sort(r), 8), np.quantile(r, (np.arange(8) + 0.5) / 8), rtol=0, atol=1e-15)
