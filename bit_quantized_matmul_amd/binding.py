@@ -1,0 +1,231 @@
+"""Thin Python binding of libbqm's C ABI (include/bqm.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libbqm.so``.  PyTorch supplies device memory and the current HIP stream.
+There is no fallback: if the library is missing or the call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbqm.so")
+
+BQM_OK, BQM_EINVAL, BQM_EALIGN, BQM_ENOTSUP, BQM_EDEVICE, BQM_ERANGE = 0, -1, -2, -3, -4, -5
+BINARY, B2, B3, B4, TERNARY = 1, 2, 3, 4, 5
+STATUS_NONFINITE, STATUS_NORM_OVERFLOW = 1, 2
+GROUP = 128
+
+EXPORTED = (
+    "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemm",
+    "q4_0_gemv", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
+)
+
+
+class BqmError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+class CqLayout(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("bits", ctypes.c_int32), ("index_bits", ctypes.c_int32), ("levels", ctypes.c_int32),
+        ("idx_row_bytes", ctypes.c_int64), ("idx_bytes", ctypes.c_int64),
+        ("norms_offset", ctypes.c_int64), ("norms_count", ctypes.c_int64),
+        ("total_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libbqm.so, raising if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m bit_quantized_matmul_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_float)
+    LP = ctypes.POINTER(CqLayout)
+    sig = {
+        "cq_pack_info": ([I, I, I, I, LP], I),
+        "cq_analytic_levels": ([I, F], I),
+        "act_fwht_quant_a8": ([P, I, I, I, P, P, P], I),
+        "cq_gemv": ([P, LP, F, P, P, I, P, P], I),
+        "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
+        "q4_0_gemv": ([P, I, I, P, I, P, P], I),
+        "cq_pack": ([P, LP, F, P, P, P], I),
+        "q4_0_pack": ([P, I, I, P, P], I),
+        "cq_codebook_fit": ([P, I64, I, I, P, P, P], I),
+        "bqm_strerror": ([I], ctypes.c_char_p),
+    }
+    for name, (args, ret) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ret
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().bqm_strerror(code).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != BQM_OK:
+        raise BqmError(fn, code)
+
+
+# ------------------------------------------------------------------ host calls
+
+def cq_pack_info(rows: int, cols: int, group: int, bits: int) -> CqLayout:
+    lay = CqLayout()
+    _check("cq_pack_info", load_library().cq_pack_info(rows, cols, group, bits, ctypes.byref(lay)))
+    return lay
+
+
+def cq_analytic_levels(bits: int) -> np.ndarray:
+    n = 2 if bits == BINARY else 3
+    out = (ctypes.c_float * 3)()
+    _check("cq_analytic_levels", load_library().cq_analytic_levels(bits, out))
+    return np.array(out[:n], dtype=np.float32)
+
+
+def _codebook_ptr(codebook):
+    """Host fp32 array (or None) -> (ctypes pointer, keep-alive object)."""
+    if codebook is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(codebook.cpu() if hasattr(codebook, "cpu") else codebook,
+                                          dtype=np.float32))
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), arr
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def act_fwht_quant_a8(x, group: int = GROUP, q=None, scale=None):
+    """x fp32 [m, k] -> (q int8 [m, k], scale fp32 [m])."""
+    torch = _torch()
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check("act_fwht_quant_a8", load_library().act_fwht_quant_a8(
+        _dev(x, torch.float32, "x"), m, k, group, _dev(q, torch.int8, "q"),
+        _dev(scale, torch.float32, "scale"), _stream()))
+    return q, scale
+
+
+def cq_gemv(blob, layout: CqLayout, codebook, q, scale, y=None):
+    """Packed CQ [rows, cols] x int8 q [batch, cols] -> fp32 y [batch, rows]."""
+    torch = _torch()
+    batch = q.shape[0]
+    if y is None:
+        y = torch.empty((batch, layout.rows), dtype=torch.float32, device=q.device)
+    cb, _keep = _codebook_ptr(codebook)
+    _check("cq_gemv", load_library().cq_gemv(
+        _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
+        _dev(scale, torch.float32, "scale"), batch, _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def cq_gemm(blob, layout: CqLayout, codebook, q, scale, y=None):
+    """Packed CQ [rows, cols] x int8 q [m, cols] -> fp32 y [m, rows] (matrix cores)."""
+    torch = _torch()
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, layout.rows), dtype=torch.float32, device=q.device)
+    cb, _keep = _codebook_ptr(codebook)
+    _check("cq_gemm", load_library().cq_gemm(
+        _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
+        _dev(scale, torch.float32, "scale"), m, _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def q4_0_gemv(blocks, rows: int, cols: int, x, y=None):
+    """Q4_0 blocks [rows, ceil(cols/32), 18] x fp32 x [batch, cols] -> fp32 y [batch, rows]."""
+    torch = _torch()
+    batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
+    _check("q4_0_gemv", load_library().q4_0_gemv(
+        _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), batch,
+        _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def cq_pack(w, layout: CqLayout, codebook, blob=None, status=None):
+    """fp32 W [rows, cols] -> packed blob (uint8 [total_bytes]) on the device."""
+    torch = _torch()
+    if blob is None:
+        blob = torch.empty((layout.total_bytes,), dtype=torch.uint8, device=w.device)
+    cb, _keep = _codebook_ptr(codebook)
+    st = _dev(status, torch.int32, "status") if status is not None else None
+    _check("cq_pack", load_library().cq_pack(
+        _dev(w, torch.float32, "w"), ctypes.byref(layout), cb, _dev(blob, torch.uint8, "blob"),
+        st, _stream()))
+    return blob
+
+
+def q4_0_nbytes(rows: int, cols: int) -> int:
+    return rows * ((cols + 31) // 32) * 18
+
+
+def q4_0_pack(w, blocks=None):
+    """fp32 W [rows, cols] -> Q4_0 blocks (uint8 [rows*ceil(cols/32)*18])."""
+    torch = _torch()
+    rows, cols = w.shape
+    if blocks is None:
+        blocks = torch.empty((q4_0_nbytes(rows, cols),), dtype=torch.uint8, device=w.device)
+    _check("q4_0_pack", load_library().q4_0_pack(
+        _dev(w, torch.float32, "w"), rows, cols, _dev(blocks, torch.uint8, "blocks"), _stream()))
+    return blocks
+
+
+def cq_codebook_fit(samples, levels: int, iters: int = 200, table=None, raw=None):
+    """Lloyd-Max fit on device fp64 samples -> (table fp32 [levels], raw fp64 [levels])."""
+    torch = _torch()
+    if table is None:
+        table = torch.empty((levels,), dtype=torch.float32, device=samples.device)
+    if raw is None:
+        raw = torch.empty((levels,), dtype=torch.float64, device=samples.device)
+    _check("cq_codebook_fit", load_library().cq_codebook_fit(
+        _dev(samples, torch.float64, "samples"), samples.numel(), levels, iters,
+        _dev(raw, torch.float64, "raw"), _dev(table, torch.float32, "table"), _stream()))
+    return table, raw

@@ -1,0 +1,289 @@
+// The C ABI of libbqm: argument checks, level tables, dispatch.
+//
+// Everything here runs on the host.  Arguments are validated before any HIP
+// call, so a rejected call touches no device.  The only state kept is a
+// per-device cache of (is gfx950, compute-unit count).
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "bqm_common.h"
+
+namespace bqm {
+
+bool cq_gemv_supported(int cols, int batch);   // cq_gemv.hip
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxFitSamples = 1024 * 512;
+
+struct DeviceInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Current device must be gfx950; returns its CU count, or a BQM error code.
+int current_device(int *num_cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BQM_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return BQM_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo &d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BQM_EDEVICE;
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.probed = true;
+  }
+  if (!d.gfx950) return BQM_ENOTSUP;
+  *num_cus = d.num_cus;
+  return BQM_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int index_bits_of(int bits) {
+  switch (bits) {
+    case BQM_CQ_BINARY: return 1;
+    case BQM_CQ_B2: return 2;
+    case BQM_CQ_B3: return 3;
+    case BQM_CQ_B4: return 4;
+    case BQM_CQ_TERNARY: return 2;
+    default: return 0;
+  }
+}
+
+int levels_of(int bits) {
+  switch (bits) {
+    case BQM_CQ_BINARY: return 2;
+    case BQM_CQ_B2: return 4;
+    case BQM_CQ_B3: return 8;
+    case BQM_CQ_B4: return 16;
+    case BQM_CQ_TERNARY: return 3;
+    default: return 0;
+  }
+}
+
+// Three-level Lloyd-Max optimum for N(0,1): c is the fixed point of
+// c = E[Z | Z >= c/2] = phi(c/2) / Q(c/2), Q the upper tail.
+double ternary_level() {
+  double c = 1.0;
+  for (int i = 0; i < 10000; ++i) {
+    const double x = 0.5 * c;
+    const double phi = exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+    const double tail = 0.5 * erfc(x / sqrt(2.0));
+    const double nxt = phi / tail;
+    if (nxt == c) break;
+    c = nxt;
+  }
+  return c;
+}
+
+// Two-level optimum for N(0,1): E|Z| = sqrt(2/pi).
+double binary_level() { return sqrt(2.0 / M_PI); }
+
+uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+bool is_bf16_exact(float f) { return (__builtin_bit_cast(uint32_t, f) & 0xFFFFu) == 0; }
+
+bool f16_exact(float f) { return (float)(_Float16)f == f; }
+
+// Build the kernels' level table.  Fitted codebooks must be finite and
+// bfloat16-representable (then they are exact in fp16 and bf16 alike).
+int make_table(int bits, const float *codebook, LevelTable *T) {
+  memset(T, 0, sizeof(*T));
+  T->bits = bits;
+  T->index_bits = index_bits_of(bits);
+  T->levels = levels_of(bits);
+  if (bits == BQM_CQ_BINARY || bits == BQM_CQ_TERNARY) {
+    if (codebook != nullptr) return BQM_EINVAL;
+    const double c = bits == BQM_CQ_BINARY ? binary_level() : ternary_level();
+    const float cf = (float)c;
+    const float sgn_bin[2] = {-1.0f, 1.0f};
+    const float sgn_ter[3] = {-1.0f, 0.0f, 1.0f};
+    const float *sg = bits == BQM_CQ_BINARY ? sgn_bin : sgn_ter;
+    for (int l = 0; l < T->levels; ++l) {
+      T->h16[l] = f32_to_f16_bits(sg[l]);
+      T->b16[l] = (uint16_t)(__builtin_bit_cast(uint32_t, sg[l]) >> 16);
+      T->f32[l] = sg[l] * cf;
+    }
+    T->cscale = cf;
+    return BQM_OK;
+  }
+  if (codebook == nullptr) return BQM_EINVAL;
+  for (int l = 0; l < T->levels; ++l) {
+    const float v = codebook[l];
+    if (!isfinite(v) || !is_bf16_exact(v) || !f16_exact(v)) return BQM_EINVAL;
+    T->h16[l] = f32_to_f16_bits(v);
+    T->b16[l] = (uint16_t)(__builtin_bit_cast(uint32_t, v) >> 16);
+    T->f32[l] = v;
+  }
+  T->cscale = 1.0f;
+  return BQM_OK;
+}
+
+int check_layout(const bqm_cq_layout *L) {
+  if (!L) return BQM_EINVAL;
+  bqm_cq_layout ref;
+  if (cq_pack_info(L->rows, L->cols, L->group, L->bits, &ref) != BQM_OK) return BQM_EINVAL;
+  if (memcmp(&ref, L, sizeof(ref)) != 0) return BQM_EINVAL;
+  if (L->group != kGroup) return BQM_ENOTSUP;
+  return BQM_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? BQM_OK : BQM_EDEVICE; }
+
+}  // namespace
+}  // namespace bqm
+
+using namespace bqm;
+
+extern "C" {
+
+int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout) {
+  if (!layout) return BQM_EINVAL;
+  const int ib = index_bits_of(bits);
+  if (ib == 0) return BQM_EINVAL;
+  if (rows < 1 || cols < 1 || group < 2 || (group & (group - 1)) != 0) return BQM_EINVAL;
+  if (cols % group != 0) return BQM_EINVAL;
+  if (((int64_t)cols * ib) % 8 != 0) return BQM_EINVAL;
+  bqm_cq_layout L;
+  memset(&L, 0, sizeof(L));
+  L.rows = rows;
+  L.cols = cols;
+  L.group = group;
+  L.bits = bits;
+  L.index_bits = ib;
+  L.levels = levels_of(bits);
+  L.idx_row_bytes = (int64_t)cols * ib / 8;
+  L.idx_bytes = (int64_t)rows * L.idx_row_bytes;
+  L.norms_offset = (L.idx_bytes + 63) / 64 * 64;
+  L.norms_count = (int64_t)rows * (cols / group);
+  L.total_bytes = (L.norms_offset + 2 * L.norms_count + 63) / 64 * 64;
+  *layout = L;
+  return BQM_OK;
+}
+
+int cq_analytic_levels(int bits, float *levels) {
+  if (!levels || (bits != BQM_CQ_BINARY && bits != BQM_CQ_TERNARY)) return BQM_EINVAL;
+  LevelTable T;
+  make_table(bits, nullptr, &T);
+  for (int l = 0; l < T.levels; ++l) levels[l] = T.f32[l];
+  return BQM_OK;
+}
+
+int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float *scale,
+                      bqm_stream_t stream) {
+  if (!x || !q || !scale || m < 1 || k < 1 || group < 2 || (group & (group - 1))) return BQM_EINVAL;
+  if (k % group) return BQM_EINVAL;
+  if (group != kGroup || k > 65536) return BQM_ENOTSUP;
+  if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scale & 3u)) return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_act_fwht_quant_a8(x, m, k, q, scale, (hipStream_t)stream));
+}
+
+int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook, const int8_t *q,
+            const float *scale, int batch, float *y, bqm_stream_t stream) {
+  if (!blob || !q || !scale || !y || batch < 1) return BQM_EINVAL;
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  LevelTable T;
+  rc = make_table(layout->bits, codebook, &T);
+  if (rc) return rc;
+  if (batch > 16 || !cq_gemv_supported(layout->cols, batch)) return BQM_ENOTSUP;
+  if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
+    return BQM_EALIGN;
+  int cus;
+  rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
+                                  (hipStream_t)stream));
+}
+
+int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook, const int8_t *q,
+            const float *scale, int m, float *y, bqm_stream_t stream) {
+  if (!blob || !q || !scale || !y || m < 1) return BQM_EINVAL;
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  LevelTable T;
+  rc = make_table(layout->bits, codebook, &T);
+  if (rc) return rc;
+  if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
+    return BQM_EALIGN;
+  int cus;
+  rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_cq_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
+                                  (hipStream_t)stream));
+}
+
+int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
+              bqm_stream_t stream) {
+  if (!blocks || !x || !y || rows < 1 || cols < 1 || batch < 1) return BQM_EINVAL;
+  if (batch > 16) return BQM_ENOTSUP;
+  if (!aligned16(blocks) || !aligned16(x) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(
+      launch_q4_0_gemv((const uint8_t *)blocks, rows, cols, x, batch, y, cus, (hipStream_t)stream));
+}
+
+int cq_pack(const float *w, const bqm_cq_layout *layout, const float *codebook, void *blob,
+            int32_t *status, bqm_stream_t stream) {
+  if (!w || !blob) return BQM_EINVAL;
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  LevelTable T;
+  rc = make_table(layout->bits, codebook, &T);
+  if (rc) return rc;
+  if (!aligned16(w) || !aligned16(blob) || ((uintptr_t)status & 3u)) return BQM_EALIGN;
+  int cus;
+  rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_cq_pack(w, *layout, T, (uint8_t *)blob, status, (hipStream_t)stream));
+}
+
+int q4_0_pack(const float *w, int rows, int cols, void *blocks, bqm_stream_t stream) {
+  if (!w || !blocks || rows < 1 || cols < 1) return BQM_EINVAL;
+  if (!aligned16(w) || !aligned16(blocks)) return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_q4_0_pack(w, rows, cols, (uint8_t *)blocks, (hipStream_t)stream));
+}
+
+int cq_codebook_fit(const double *samples, int64_t n, int levels, int iters, double *raw,
+                    float *table, bqm_stream_t stream) {
+  if (!samples || !table || n < 2 || iters < 0) return BQM_EINVAL;
+  if (levels != 2 && levels != 4 && levels != 8 && levels != 16) return BQM_EINVAL;
+  if (n > kMaxFitSamples) return BQM_ENOTSUP;
+  if (((uintptr_t)samples & 7u) || ((uintptr_t)raw & 7u) || ((uintptr_t)table & 3u))
+    return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_codebook_fit(samples, n, levels, iters, raw, table, (hipStream_t)stream));
+}
+
+const char *bqm_strerror(int code) {
+  switch (code) {
+    case BQM_OK: return "ok";
+    case BQM_EINVAL: return "invalid argument";
+    case BQM_EALIGN: return "misaligned pointer";
+    case BQM_ENOTSUP: return "not supported";
+    case BQM_EDEVICE: return "device error";
+    case BQM_ERANGE: return "value out of range";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Per-token symmetric int8 activations after the group FWHT.
+//
+// "14MB holds 45M parameters: dissecting Needle's .cact file and W4A8
+// quantization", section 1: activations are 8-bit (W4A8) and each weight group
+// is rotated by the orthogonal normalized Walsh-Hadamard matrix, so
+// dot(w_g, x_g) = norm_g/G * dot(cb[idx_g], H_u x_g): the activation is
+// rotated once here and the weights are never transformed back.
+//
+// One workgroup per token row.  Each lane owns 8 consecutive elements of a
+// 128-wide group; 16 lanes hold one group.  Butterfly stages of half-width
+// 1, 2, 4 are inside a lane, 8..64 across lanes (partner lane = lane ^ (h/8)).
+// Every stage computes (a+b, a-b) for the pair (j, j+h), j the lower index,
+// in fp32, so the result is bit-identical to any fp32 evaluation of the same
+// network.  Then s = max|u| / 127 over the row (1 for a zero row) and
+// q = clip(rint(u / s), -127, 127), both divisions correctly rounded.
+#include "bqm_common.h"
+
+namespace bqm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerLane = 8;
+constexpr int kMaxChunksPerThread = 32;   // k <= 256 * 8 * 32 = 65536
+
+// u / s with IEEE round-to-nearest-even (HIP's default fp32 division is
+// correctly rounded; spelled out so the intent survives compiler flags).
+__device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
+
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
+    const float *__restrict__ x, int k, int8_t *__restrict__ q, float *__restrict__ scale) {
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int chunks = k / kPerLane;           // 8-element chunks in the row
+  const float *xr = x + (size_t)row * k;
+
+  float v[CPT][kPerLane];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = t + c * kThreads;
+    if (ci < chunks) {
+      const float4 a = *reinterpret_cast<const float4 *>(xr + ci * kPerLane);
+      const float4 b = *reinterpret_cast<const float4 *>(xr + ci * kPerLane + 4);
+      v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
+      v[c][4] = b.x; v[c][5] = b.y; v[c][6] = b.z; v[c][7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) v[c][e] = 0.0f;
+    }
+    // in-lane stages h = 1, 2, 4
+#pragma unroll
+    for (int h = 1; h < kPerLane; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        if ((j & h) == 0) {
+          const float a = v[c][j], b = v[c][j + h];
+          v[c][j] = a + b;
+          v[c][j + h] = a - b;
+        }
+      }
+    }
+    // cross-lane stages h = 8 .. 64: partner lane differs in bit (h/8) of lane%16.
+    // Chunks with ci >= chunks belong to whole groups past the row end (k is a
+    // multiple of 128 and 16 lanes hold one group), so their lanes exchange
+    // only with each other.
+#pragma unroll
+    for (int hl = 1; hl < 16; hl <<= 1) {
+      const bool upper = (lane & hl) != 0;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        const float other = __shfl_xor(v[c][e], hl, 64);
+        v[c][e] = upper ? (other - v[c][e]) : (v[c][e] + other);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+  }
+
+  __shared__ float red[kThreads / kWave];
+  __shared__ float s_shared;
+  amax = wave_max(amax);
+  if (lane == 0) red[t >> 6] = amax;
+  __syncthreads();
+  if (t == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) m = fmaxf(m, red[w]);
+    const float s = (m > 0.0f) ? div_rn(m, 127.0f) : 1.0f;
+    s_shared = s;
+    scale[row] = s;
+  }
+  __syncthreads();
+  const float s = s_shared;
+
+  int8_t *qr = q + (size_t)row * k;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = t + c * kThreads;
+    if (ci < chunks) {
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        float r = rintf(div_rn(v[c][e], s));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const uint32_t byte = (uint32_t)(uint8_t)(int8_t)(int)r;
+        packed[e >> 2] |= byte << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2 *>(qr + ci * kPerLane) = make_uint2(packed[0], packed[1]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_fwht_quant_a8(const float *x, int m, int k, int8_t *q, float *scale,
+                                    hipStream_t s) {
+  const int chunks = k / kPerLane;
+  const int cpt = (chunks + kThreads - 1) / kThreads;
+  dim3 grid(m), block(kThreads);
+  if (cpt <= 1)
+    act_fwht_quant_a8_kernel<1><<<grid, block, 0, s>>>(x, k, q, scale);
+  else if (cpt <= 2)
+    act_fwht_quant_a8_kernel<2><<<grid, block, 0, s>>>(x, k, q, scale);
+  else if (cpt <= 4)
+    act_fwht_quant_a8_kernel<4><<<grid, block, 0, s>>>(x, k, q, scale);
+  else if (cpt <= 8)
+    act_fwht_quant_a8_kernel<8><<<grid, block, 0, s>>>(x, k, q, scale);
+  else if (cpt <= 16)
+    act_fwht_quant_a8_kernel<16><<<grid, block, 0, s>>>(x, k, q, scale);
+  else
+    act_fwht_quant_a8_kernel<kMaxChunksPerThread><<<grid, block, 0, s>>>(x, k, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace bqm

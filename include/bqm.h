@@ -1,0 +1,170 @@
+/*
+ * bqm.h -- weight-only low-bit quantized matmul on MI355X (gfx950).
+ *
+ * C ABI of libbqm.so.  Plain pointers and sizes only.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [device] are HIP device memory owned by the caller (for
+ *     example a torch tensor's data pointer); pointers marked [host] are host
+ *     memory owned by the caller.  The library never allocates or frees
+ *     memory and keeps no state beyond cached per-device properties.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL means the default stream).  Results are valid once the stream has
+ *     been synchronized.  Calls that share buffers must be ordered by the
+ *     caller (same stream or events).
+ *   - Every argument is validated on the host before anything is launched.
+ *     The return value is BQM_OK (0) or a negative BQM_E* code; on error
+ *     nothing has been enqueued.  BQM_EDEVICE reports a HIP error seen while
+ *     launching (hipGetLastError).
+ *   - Matrices are row-major.  Weight matrices are [out, in] = [rows, cols]:
+ *     every output row is contiguous along the reduction axis and quant
+ *     groups run along that axis ("14MB holds 45M parameters: dissecting
+ *     Needle's .cact file and W4A8 quantization", section 3).
+ *   - Only gfx950 devices are accepted (BQM_ENOTSUP otherwise).
+ */
+#ifndef BQM_H
+#define BQM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *bqm_stream_t; /* a hipStream_t */
+
+enum {
+  BQM_OK = 0,
+  BQM_EINVAL = -1,  /* null pointer, bad shape, unknown bits code, bad codebook */
+  BQM_EALIGN = -2,  /* a device pointer is not 16-byte aligned                 */
+  BQM_ENOTSUP = -3, /* valid request the device path does not provide
+                       (group != 128, batch > 16, non-gfx950 device)           */
+  BQM_EDEVICE = -4, /* HIP reported an error while launching                   */
+  BQM_ERANGE = -5   /* reported through an encoder's status word, see cq_pack  */
+};
+
+/* CQ bits codes, as the pages number them: 2/3/4 index the fitted codebooks
+ * cb2/cb3/cb4 (4, 8, 16 levels); 5 is ternary {-c, 0, +c} and 1 binary
+ * {-sqrt(2/pi), +sqrt(2/pi)}, both analytic and built into the library
+ * ("Parse-free loading: mmap tensors and Needle's cold start", passage on
+ * the CQ format). */
+enum { BQM_CQ_BINARY = 1, BQM_CQ_B2 = 2, BQM_CQ_B3 = 3, BQM_CQ_B4 = 4, BQM_CQ_TERNARY = 5 };
+
+/* Status-word bits written by the encoders (OR-ed, never cleared). */
+enum { BQM_STATUS_NONFINITE = 1, BQM_STATUS_NORM_OVERFLOW = 2 };
+
+/* Byte layout of one packed CQ matrix ("blob"):
+ *   [0, idx_bytes)            index rows back to back, idx_row_bytes each; a
+ *                             row is an LSB-first stream of index_bits-wide
+ *                             fields (index j at bits [b*j, b*j+b)), so 8
+ *                             indices fill exactly index_bits bytes and, for
+ *                             4 bits, the low nibble of a byte is the even
+ *                             column (Needle article, section 1);
+ *   [norms_offset, +2*norms_count)  fp16 group L2 norms [rows][cols/group];
+ *   total_bytes               rounded up to 64 (the .cact 64-byte blob
+ *                             alignment, Needle article, section 2).
+ * Ternary uses 2-bit fields holding 0/1/2 (field value 3 decodes to 0). */
+typedef struct {
+  int32_t rows, cols, group, bits, index_bits, levels;
+  int64_t idx_row_bytes, idx_bytes, norms_offset, norms_count, total_bytes;
+} bqm_cq_layout;
+
+/* Fill `layout` [host] for a rows x cols matrix, quant group `group` (a power
+ * of two >= 2 dividing cols) and bits code `bits`.  Host only, no device
+ * access.  BQM_EINVAL on a bad shape, group or code. */
+int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout);
+
+/* Built-in levels of the analytic sets: bits 1 -> 2 values, bits 5 -> 3
+ * values, ascending fp32, written to `levels` [host].  BQM_EINVAL for other
+ * codes.  Host only. */
+int cq_analytic_levels(int bits, float *levels);
+
+/* Per-token symmetric int8 activations in the rotated domain
+ * (Needle article, section 1: W4A8; the rotation H is orthogonal, so
+ * dot(w_g, x_g) = norm_g/G * dot(cb[idx_g], H_u x_g) and only x is rotated).
+ * x [device] fp32 [m, k]; q [device] int8 [m, k]; scale [device] fp32 [m].
+ * Per row: u = H_u x_g for each group of `group` columns (unnormalized
+ * Sylvester-order butterfly, stages of half-width 1, 2, ..., group/2),
+ * s = max|u| / 127 (1 for an all-zero row), q = clip(rint(u / s), -127, 127)
+ * with correctly rounded fp32 division and half-even rounding.
+ * Requires k % group == 0, group == 128, k <= 65536, x and q 16-byte aligned. */
+int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float *scale,
+                      bqm_stream_t stream);
+
+/* Decode GEMV on packed CQ weights (Needle article, section 3: decode is a
+ * GEMV streaming [out, in] rows; dequantization happens inside the kernel).
+ *   y[b, n] = scale[b] / G * sum_g norm[n, g] * sum_{i in g} cb[idx[n, i]] * q[b, i]
+ * blob [device] packed as `layout` [host] describes (16-byte aligned);
+ * codebook [host] `layout->levels` fp32 values for bits 2/3/4, index order
+ * (each finite and bfloat16-representable, hence exact in fp16 too;
+ * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
+ * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
+ * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128. */
+int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+            const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
+
+/* Prefill GEMM on packed CQ weights (Needle article, section 3: prefill is a
+ * GEMM with the same layout, every row one reduction stream).  Same sum as
+ * cq_gemv for m tokens: q [device] int8 [m, cols], scale [device] fp32 [m],
+ * y [device] fp32 [m, rows].  The weight tile is dequantized to bfloat16
+ * codebook values (exact: the codebook is bfloat16-representable) and
+ * multiplied on the matrix cores with fp32 accumulation; the group norm and
+ * token scale are applied in fp32.  m >= 1, group must be 128. */
+int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+            const int8_t *q, const float *scale, int m, float *y, bqm_stream_t stream);
+
+/* Q4_0 GEMV (Minueza-32M -> KMCU v1 page, sections 2 and 3).
+ * blocks [device]: rows * ceil(cols/32) blocks of 18 bytes, row-major, each
+ * block = fp16 scale d (little-endian) then 16 bytes of 4-bit codes, the low
+ * nibble the even element; weight = (nibble - 8) * d; rows are zero-padded to
+ * a multiple of 32 so a block never straddles two rows.
+ * x [device] fp32 [batch, cols] (no padding needed: columns >= cols are never
+ * read); y [device] fp32 [batch, rows].  1 <= batch <= 16. */
+int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
+              bqm_stream_t stream);
+
+/* Encode fp32 weights into a CQ blob on the device (Needle article,
+ * section 1: group FWHT with the normalized Walsh-Hadamard matrix, nearest
+ * Lloyd-Max level per coordinate, fp16 group L2 norm, LSB-first packing).
+ * Computed in fp64 without fused multiply-adds, in the order:
+ *   u = H_u w (butterfly); ss = sum_i u_i*u_i (i ascending); r = sqrt(ss);
+ *   norm = fp16_rne(r / sqrt(G)); t_i = u_i * (sqrt(G) / r) (0 if r == 0);
+ *   idx_i = argmin_l |t_i - cb_l| (lower l on a tie);
+ * so it is bit-exact with a reference that performs the same operations.
+ * w [device] fp32 [rows, cols]; codebook [host] as for cq_gemv; blob [device]
+ * layout->total_bytes (16-byte aligned; padding bytes are written as zero).
+ * status [device, may be NULL] int32 word OR-ed with BQM_STATUS_NONFINITE for
+ * a non-finite weight and BQM_STATUS_NORM_OVERFLOW when a norm exceeds fp16;
+ * the caller zeroes it beforehand and reads it after synchronizing. */
+int cq_pack(const float *w, const bqm_cq_layout *layout, const float *codebook, void *blob,
+            int32_t *status, bqm_stream_t stream);
+
+/* Encode fp32 weights into Q4_0 blocks (Minueza page, sections 2 and 3):
+ * pad each row to a multiple of 32, per block amax = max|w|, d = amax/8
+ * (1 when amax == 0), q = clip(rint(w/d), -8, 7) with correctly rounded fp32
+ * division, nibble = q + 8, block = fp16(d) then nibbles (low = even).
+ * w [device] fp32 [rows, cols]; blocks [device] rows*ceil(cols/32)*18 bytes. */
+int q4_0_pack(const float *w, int rows, int cols, void *blocks, bqm_stream_t stream);
+
+/* Lloyd-Max codebook fit on the device (Needle article, section 1: 400k
+ * Gaussian samples, 200 iterations; cb2/cb3/cb4).  One workgroup:
+ *   fold to |z|; start the levels/2 positive levels at the interpolated order
+ *   statistics (i + 1/2)/(levels/2); each iteration sets cell boundaries at
+ *   midpoints of adjacent levels and moves each level to its cell mean (sums
+ *   taken over blocks of 512 samples in order, then the block sums in order;
+ *   an empty cell keeps its level); mirror to `levels` ascending values.
+ * samples [device] fp64 [n] (2 <= n <= 524288, BQM_ENOTSUP above: one
+ * workgroup of 1024 threads owns blocks of 512); levels in {2, 4, 8, 16};
+ * raw [device, may be NULL] fp64 [levels] unrounded result; table [device]
+ * fp32 [levels] each value rounded half-even to bfloat16 precision. */
+int cq_codebook_fit(const double *samples, int64_t n, int levels, int iters, double *raw,
+                    float *table, bqm_stream_t stream);
+
+/* Human-readable name of an error code (static string). */
+const char *bqm_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQM_H */

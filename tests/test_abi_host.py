@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import codebook as ocb
+from oracle import cq as ocq
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bqm.h")
+
+
+def declared_functions() -> list[str]:
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_matmul_amd import binding
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libbqm.so is not built (run python -m bit_quantized_matmul_amd.build)")
+    return binding.load_library()
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for required in ("cq_pack_info", "act_fwht_quant_a8", "cq_gemv", "cq_gemm", "q4_0_gemv",
+                     "cq_pack", "q4_0_pack", "cq_codebook_fit", "cq_analytic_levels", "bqm_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from bit_quantized_matmul_amd import binding
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), f"libbqm.so does not export {n}"
+    assert set(names) == set(binding.EXPORTED)
+
+
+@pytest.mark.parametrize("rows,cols,code", [(512, 512, 4), (14336, 4096, 4), (104, 1024, 3), (7, 256, 1),
+                                            (5, 384, 5), (4096, 14336, 2), (1, 128, 3)])
+def test_pack_info_matches_oracle(lib, rows, cols, code):
+    from bit_quantized_matmul_amd import binding
+    assert binding.cq_pack_info(rows, cols, 128, code).as_dict() == ocq.pack_info(rows, cols, 128, code)
+
+
+def test_pack_info_rejects_bad_arguments(lib):
+    from bit_quantized_matmul_amd import binding
+    lay = binding.CqLayout()
+    for args in [(4, 100, 128, 4), (4, 128, 128, 6), (0, 128, 128, 4), (4, 128, 96, 4), (4, 128, 128, 0)]:
+        assert lib.cq_pack_info(*args, ctypes.byref(lay)) == binding.BQM_EINVAL
+    assert lib.cq_pack_info(4, 128, 128, 4, None) == binding.BQM_EINVAL
+
+
+def test_analytic_levels_match_oracle(lib):
+    from bit_quantized_matmul_amd import binding
+    assert np.array_equal(binding.cq_analytic_levels(1), ocb.analytic_levels(1))
+    assert np.array_equal(binding.cq_analytic_levels(5), ocb.analytic_levels(5))
+    out = (ctypes.c_float * 3)()
+    assert lib.cq_analytic_levels(4, out) == binding.BQM_EINVAL
+
+
+def test_device_entry_points_validate_before_touching_a_device(lib):
+    """Invalid calls return an error code; none of them reaches HIP (no GPU here)."""
+    from bit_quantized_matmul_amd import binding
+    lay = binding.cq_pack_info(256, 512, 128, 4)
+    bad = binding.cq_pack_info(256, 512, 128, 4)
+    bad.idx_bytes += 1                                  # inconsistent layout
+    cb = (ctypes.c_float * 16)(*([0.5] * 16))
+    p = ctypes.c_void_p(4096)                           # never dereferenced: checks fail first
+    E = binding
+    assert lib.act_fwht_quant_a8(None, 1, 128, 128, p, p, None) == E.BQM_EINVAL
+    assert lib.act_fwht_quant_a8(p, 1, 100, 128, p, p, None) == E.BQM_EINVAL
+    assert lib.act_fwht_quant_a8(p, 1, 256, 64, p, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv(p, ctypes.byref(bad), cb, p, p, 1, p, None) == E.BQM_EINVAL
+    assert lib.cq_gemv(p, ctypes.byref(lay), None, p, p, 1, p, None) == E.BQM_EINVAL   # codebook needed
+    assert lib.cq_gemv(p, ctypes.byref(lay), cb, p, p, 0, p, None) == E.BQM_EINVAL
+    assert lib.cq_gemv(p, ctypes.byref(lay), cb, p, p, 17, p, None) == E.BQM_ENOTSUP
+    nonbf16 = (ctypes.c_float * 16)(*([0.1] * 16))     # 0.1 is not bfloat16-representable
+    assert lib.cq_gemv(p, ctypes.byref(lay), nonbf16, p, p, 1, p, None) == E.BQM_EINVAL
+    tern = binding.cq_pack_info(256, 512, 128, 5)
+    assert lib.cq_gemv(p, ctypes.byref(tern), cb, p, p, 1, p, None) == E.BQM_EINVAL     # analytic: NULL
+    g64 = binding.cq_pack_info(256, 512, 64, 4)
+    assert lib.cq_gemm(p, ctypes.byref(g64), cb, p, p, 4, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv(ctypes.c_void_p(4097), ctypes.byref(lay), cb, p, p, 1, p, None) == E.BQM_EALIGN
+    assert lib.q4_0_gemv(None, 4, 312, p, 1, p, None) == E.BQM_EINVAL
+    assert lib.q4_0_gemv(p, 4, 312, p, 17, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL
+    assert lib.q4_0_pack(p, 0, 312, p, None) == E.BQM_EINVAL
+    assert lib.cq_codebook_fit(p, 1 << 20, 16, 200, None, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_codebook_fit(p, 1000, 6, 200, None, p, None) == E.BQM_EINVAL
+    assert binding.strerror(E.BQM_EALIGN) == "misaligned pointer"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from bit_quantized_matmul_amd import binding
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library()
