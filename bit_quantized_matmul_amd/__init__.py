@@ -8,7 +8,7 @@ workloads) can be imported without the library.
 from __future__ import annotations
 
 __all__ = [
-    "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemm",
+    "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32", "cq_gemm",
     "q4_0_gemv", "cq_pack", "q4_0_pack", "cq_codebook_fit", "CqLayout", "BqmError",
 ]
 

@@ -20,8 +20,8 @@ STATUS_NONFINITE, STATUS_NORM_OVERFLOW = 1, 2
 GROUP = 128
 
 EXPORTED = (
-    "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemm",
-    "q4_0_gemv", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
+    "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
+    "cq_gemm", "q4_0_gemv", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
 )
 
 
@@ -67,6 +67,7 @@ def load_library() -> ctypes.CDLL:
         "cq_analytic_levels": ([I, F], I),
         "act_fwht_quant_a8": ([P, I, I, I, P, P, P], I),
         "cq_gemv": ([P, LP, F, P, P, I, P, P], I),
+        "cq_gemv_f32": ([P, LP, F, P, I, P, P, P, P], I),
         "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
         "q4_0_gemv": ([P, I, I, P, I, P, P], I),
         "cq_pack": ([P, LP, F, P, P, P], I),
@@ -162,6 +163,22 @@ def cq_gemv(blob, layout: CqLayout, codebook, q, scale, y=None):
     _check("cq_gemv", load_library().cq_gemv(
         _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
         _dev(scale, torch.float32, "scale"), batch, _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def cq_gemv_f32(blob, layout: CqLayout, codebook, x, y=None, q_out=None, scale_out=None):
+    """Packed CQ [rows, cols] x fp32 x [batch, cols] -> fp32 y [batch, rows]; the A8
+    step runs inside the GEMV launch (optional q_out / scale_out receive the codes)."""
+    torch = _torch()
+    batch = x.shape[0]
+    if y is None:
+        y = torch.empty((batch, layout.rows), dtype=torch.float32, device=x.device)
+    cb, _keep = _codebook_ptr(codebook)
+    qo = _dev(q_out, torch.int8, "q_out") if q_out is not None else None
+    so = _dev(scale_out, torch.float32, "scale_out") if scale_out is not None else None
+    _check("cq_gemv_f32", load_library().cq_gemv_f32(
+        _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(x, torch.float32, "x"),
+        batch, _dev(y, torch.float32, "y"), qo, so, _stream()))
     return y
 
 

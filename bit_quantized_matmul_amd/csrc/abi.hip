@@ -12,7 +12,7 @@
 
 namespace bqm {
 
-bool cq_gemv_supported(int cols, int batch);   // cq_gemv.hip
+bool cq_gemv_supported(int cols, int batch, bool fused);   // cq_gemv.hip
 
 namespace {
 
@@ -198,7 +198,7 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  if (batch > 16 || !cq_gemv_supported(layout->cols, batch)) return BQM_ENOTSUP;
+  if (batch > 16 || !cq_gemv_supported(layout->cols, batch, false)) return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;
   int cus;
@@ -206,6 +206,26 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   if (rc) return rc;
   return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
                                   (hipStream_t)stream));
+}
+
+int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+                const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
+                bqm_stream_t stream) {
+  if (!blob || !x || !y || batch < 1) return BQM_EINVAL;
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  LevelTable T;
+  rc = make_table(layout->bits, codebook, &T);
+  if (rc) return rc;
+  if (batch > 16 || !cq_gemv_supported(layout->cols, batch, true)) return BQM_ENOTSUP;
+  if (!aligned16(blob) || !aligned16(x) || ((uintptr_t)q_out & 3u) || ((uintptr_t)scale_out & 3u) ||
+      ((uintptr_t)y & 3u))
+    return BQM_EALIGN;
+  int cus;
+  rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_cq_gemv_f32((const uint8_t *)blob, *layout, T, x, batch, y, q_out,
+                                      scale_out, cus, (hipStream_t)stream));
 }
 
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook, const int8_t *q,

@@ -18,9 +18,27 @@
 namespace bqm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kPerLane = 8;
-constexpr int kMaxChunksPerThread = 32;   // k <= 256 * 8 * 32 = 65536
+constexpr int kMaxChunksPerThread = 8;    // k <= 1024 * 8 * 8 = 65536
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
+
+// max over the wave (values are >= 0, so a 0 from an inactive DPP source is
+// harmless); the result is valid in lanes 48..63.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0x121, 0xF>(v));
+  v = fmaxf(v, dpp_f<0x122, 0xF>(v));
+  v = fmaxf(v, dpp_f<0x124, 0xF>(v));
+  v = fmaxf(v, dpp_f<0x128, 0xF>(v));
+  v = fmaxf(v, dpp_f<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_f<0x143, 0xC>(v));
+  return v;
+}
 
 // u / s with IEEE round-to-nearest-even (HIP's default fp32 division is
 // correctly rounded; spelled out so the intent survives compiler flags).
@@ -80,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
 
   __shared__ float red[kThreads / kWave];
   __shared__ float s_shared;
-  amax = wave_max(amax);
-  if (lane == 0) red[t >> 6] = amax;
+  amax = wave_max_dpp(amax);
+  if (lane == 63) red[t >> 6] = amax;
   __syncthreads();
   if (t == 0) {
     float m = red[0];
@@ -125,10 +143,6 @@ hipError_t launch_act_fwht_quant_a8(const float *x, int m, int k, int8_t *q, flo
     act_fwht_quant_a8_kernel<2><<<grid, block, 0, s>>>(x, k, q, scale);
   else if (cpt <= 4)
     act_fwht_quant_a8_kernel<4><<<grid, block, 0, s>>>(x, k, q, scale);
-  else if (cpt <= 8)
-    act_fwht_quant_a8_kernel<8><<<grid, block, 0, s>>>(x, k, q, scale);
-  else if (cpt <= 16)
-    act_fwht_quant_a8_kernel<16><<<grid, block, 0, s>>>(x, k, q, scale);
   else
     act_fwht_quant_a8_kernel<kMaxChunksPerThread><<<grid, block, 0, s>>>(x, k, q, scale);
   return hipGetLastError();

@@ -103,6 +103,18 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
+/* Decode GEMV from fp32 activations: act_fwht_quant_a8 followed by cq_gemv in
+ * one launch (same results bit for bit).  Every workgroup quantizes the
+ * activations itself while its first weight loads are in flight, so there is
+ * no separate activation launch on the decode path.  x [device] fp32
+ * [batch, cols], 16-byte aligned; y [device] fp32 [batch, rows]; q_out
+ * [device, may be NULL] int8 [batch, cols] and scale_out [device, may be
+ * NULL] fp32 [batch] receive the int8 codes and scales.  Other arguments and
+ * limits as cq_gemv, and cols <= 16384. */
+int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+                const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
+                bqm_stream_t stream);
+
 /* Prefill GEMM on packed CQ weights (Needle article, section 3: prefill is a
  * GEMM with the same layout, every row one reduction stream).  Same sum as
  * cq_gemv for m tokens: q [device] int8 [m, cols], scale [device] fp32 [m],

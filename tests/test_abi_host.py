@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for required in ("cq_pack_info", "act_fwht_quant_a8", "cq_gemv", "cq_gemm", "q4_0_gemv",
+    for required in ("cq_pack_info", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32", "cq_gemm", "q4_0_gemv",
                      "cq_pack", "q4_0_pack", "cq_codebook_fit", "cq_analytic_levels", "bqm_strerror"):
         assert required in names
 
@@ -90,6 +90,10 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     g64 = binding.cq_pack_info(256, 512, 64, 4)
     assert lib.cq_gemm(p, ctypes.byref(g64), cb, p, p, 4, p, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv(ctypes.c_void_p(4097), ctypes.byref(lay), cb, p, p, 1, p, None) == E.BQM_EALIGN
+    big = binding.cq_pack_info(8, 32768, 128, 4)
+    assert lib.cq_gemv_f32(p, ctypes.byref(big), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
+    assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
     assert lib.q4_0_gemv(None, 4, 312, p, 1, p, None) == E.BQM_EINVAL
     assert lib.q4_0_gemv(p, 4, 312, p, 17, p, None) == E.BQM_ENOTSUP
     assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL

@@ -144,6 +144,37 @@ def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
 
 
 @pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
+                                             (1024, 4096, 1), (70, 4096, 4), (33, 1024, 16),
+                                             (5, 128, 2), (1, 256, 1), (200, 4096, 3)])
+def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
+    """One-launch A8 + GEMV: the codes and scales equal the oracle's bit for bit and y
+    equals the two-launch path (act_fwht_quant_a8, then cq_gemv) bit for bit."""
+    rng = np.random.default_rng(450 + code * 13 + rows + batch)
+    w = weights(rng, rows, cols)
+    x = inputs.activations(rng, batch, cols)
+    if batch > 1:
+        x[1] = 0.0                                       # zero token: s = 1, codes 0
+    lv = levels(code, codebooks)
+    idx, n16 = ocq.encode(w, 128, code, lv)
+    blob = dev(ocq.make_blob(idx, n16, 128, code))
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    cb = host_codebook(code, codebooks)
+    dx = dev(x)
+    q_out = torch.empty((batch, cols), dtype=torch.int8, device=DEV)
+    s_out = torch.empty((batch,), dtype=torch.float32, device=DEV)
+    y1 = host(B.cq_gemv_f32(blob, lay, cb, dx, q_out=q_out, scale_out=s_out))
+    q, s = B.act_fwht_quant_a8(dx)
+    y2 = host(B.cq_gemv(blob, lay, cb, q, s))
+    q_ref, s_ref = oa8.act_quant_a8(x, 128, "fp32")
+    assert np.array_equal(host(q_out), q_ref)
+    assert np.array_equal(host(s_out).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    ref = omm.cq_reference(idx, n16, 128, code, lv, q_ref, s_ref)
+    assert omm.rel_l2(y1, ref) <= TOL
+
+
+@pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("m,rows,cols", [(37, 300, 512), (128, 256, 1024), (1, 100, 128),
                                          (200, 130, 384), (257, 64, 256)])
 def test_cq_gemm_parity(code, m, rows, cols, codebooks):
