@@ -52,7 +52,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "sweep", "copy"])
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
+
+
+EAGER = False
 
 
 class Timer:
@@ -76,7 +81,18 @@ class Timer:
 def graph_mean_ms(torch, launches, reps: int = 3) -> float:
     """Mean duration per launch of `launches` captured once in a HIP graph and
     replayed `reps` times between one HIP event pair on the launch stream (no
-    host launch overhead between the kernels)."""
+    host launch overhead between the kernels).  With --no-graph the sequence is
+    launched eagerly instead (host-bound for short kernels)."""
+    if EAGER:
+        for fn in launches:
+            fn()
+        torch.cuda.synchronize()
+        t = Timer()
+        t.start()
+        for _ in range(reps):
+            for fn in launches:
+                fn()
+        return t.stop_ms() / (reps * len(launches))
     for fn in launches[:2]:
         fn()                                     # warm caches of device properties
     torch.cuda.synchronize()
@@ -417,7 +433,9 @@ def traffic_for_dominant():
 
 
 def main():
+    global EAGER
     args = parse()
+    EAGER = args.no_graph
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -40,7 +40,9 @@ def hipcc() -> str:
 
 
 def sources() -> list[str]:
-    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """All HIP sources, the long compiles (GEMV kernel sets, GEMM) first."""
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(srcs, key=lambda f: (not f.startswith("cq_gemv_i"), f != "cq_gemm.hip", f))
 
 
 def _compile(src: str) -> str:

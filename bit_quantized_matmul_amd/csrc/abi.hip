@@ -12,7 +12,7 @@
 
 namespace bqm {
 
-bool cq_gemv_supported(int cols, int batch, bool fused);   // cq_gemv.hip
+bool cq_gemv_supported(const bqm_cq_layout &L, bool fused);   // cq_gemv.hip
 
 namespace {
 
@@ -198,7 +198,7 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  if (batch > 16 || !cq_gemv_supported(layout->cols, batch, false)) return BQM_ENOTSUP;
+  if (batch > 16 || !cq_gemv_supported(*layout, false)) return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;
   int cus;
@@ -217,7 +217,7 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  if (batch > 16 || !cq_gemv_supported(layout->cols, batch, true)) return BQM_ENOTSUP;
+  if (batch > 16 || !cq_gemv_supported(*layout, true)) return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(x) || ((uintptr_t)q_out & 3u) || ((uintptr_t)scale_out & 3u) ||
       ((uintptr_t)y & 3u))
     return BQM_EALIGN;
