@@ -38,7 +38,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 matrix, published
 POOL_BYTES = 1 << 30             # >= 1 GiB of distinct weight copies per measurement
 METRIC = "decode GEMV effective weight GB/s (% of HBM peak); prefill GEMM TFLOP/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cq_gemv_4096x14336_traffic.json")
-GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matmul_amd", "csrc", "cq_gemv.hip")
+GEMV_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_amd", "csrc", f)
+                for f in ("cq_gemv_impl.h", "cq_gemv_i4f.hip")]
 
 
 def log(msg: str) -> None:
@@ -424,7 +425,7 @@ def traffic_for_dominant():
         return None
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        digest = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
+        digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in GEMV_SOURCES)).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
         return float(rec["bytes_per_launch"])
