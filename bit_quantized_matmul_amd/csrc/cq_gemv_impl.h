@@ -231,7 +231,8 @@ struct GemvArgs {
 // rint(u * inv) unless u * inv lies within 1e-4 of a half-integer: for
 // |u / s| <= 127 the product differs from the correctly rounded quotient by at
 // most 2.3e-5, so away from the rounding boundaries both give the same
-// integer.  Near a boundary (rare) the quotient is taken exactly.
+// integer.  Near a boundary (rare) the quotient is taken exactly.  (The clip
+// binds only when amax / 127 underflows to zero.)
 template <int N>
 __device__ __forceinline__ void a8_codes(const float (&u)[N], float s, float inv, float (&code)[N]) {
   bool near = false;
@@ -483,20 +484,25 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       if (lane == 63) amax_red[b * kWaves + wave] = mx;
     }
     __syncthreads();
-    if (t < BATCH) {
-      float mx = amax_red[t * kWaves];
-      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, amax_red[t * kWaves + w]);
-      const float sc = (mx > 0.0f) ? __fdiv_rn(mx, 127.0f) : 1.0f;
-      s_blk[t] = sc;
-      s_blk[BATCH + t] = 1.0f / sc;
+    // every wave forms the scales itself (same values, no second barrier)
+    float scs[BATCH], invs[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      float mx = amax_red[b * kWaves];
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, amax_red[b * kWaves + w]);
+      scs[b] = (mx > 0.0f) ? __fdiv_rn(mx, 127.0f) : 1.0f;
+      invs[b] = 1.0f / scs[b];
     }
-    __syncthreads();
+    if (t < BATCH) s_blk[t] = scs[t];
 #pragma unroll
     for (int j = 0; j < SEGS; ++j) {
       const int sg = t + j * kThreads;
       if (sg < nseg) {
         const int b = sg / spr, c = sg - b * spr;
-        const float sc = s_blk[b], inv = s_blk[BATCH + b];
+        float sc = scs[0], inv = invs[0];
+#pragma unroll
+        for (int bb = 1; bb < BATCH; ++bb)
+          if (b == bb) { sc = scs[bb]; inv = invs[bb]; }
         // codes in blocks of 8 (bounded register use), packed to fp16 pairs
         uint32_t pr[16];
 #pragma unroll
@@ -669,8 +675,11 @@ struct GemvConfig {
 
 // Lanes per row slot P (a power of two up to 64), chunks per lane per work
 // item CPL (1, 2 or 4), parts per row NP and waves per row S, so that
-// P * CPL * NP * S covers the row's C chunks.  The K split S is used only
-// when rows are too few to give the GPU's waves work; it needs NP == 1.
+// P * CPL * NP * S covers the row's C chunks.  Preferred: the smallest K split
+// S that leaves a lane at most two chunks of a row (one work item per row, the
+// activations in registers) while the rows still give every wave work.
+// Measured on MI355X at the 8B-class decode shapes, this beats longer rows
+// per wave (more parts, activations re-read from LDS) by 15-30%.
 bool choose_config(int rows, int C, int batch, int num_cus, GemvConfig &cfg) {
   const int waves_total = num_cus * 8;
   const int max_cpl = batch >= 4 ? 2 : 4;
@@ -682,27 +691,17 @@ bool choose_config(int rows, int C, int batch, int num_cus, GemvConfig &cfg) {
     const int rpw = kWave / P;
     const long wave_rows = ((long)rows * S + rpw - 1) / rpw;
     if (S < 8 && wave_rows < waves_total) continue;      // too little parallelism: split K
+    if (S < 8 && slots > 2) continue;                     // long rows: split K further
     int cpl = slots <= 1 ? 1 : (slots <= 2 ? 2 : 4);
     if (cpl > max_cpl) cpl = max_cpl;
-    const int nparts = (slots + cpl - 1) / cpl;
-    if (S > 1 && nparts > 1) continue;
     cfg.plog2 = plog2;
     cfg.cpl = cpl;
     cfg.S = S;
-    cfg.nparts = nparts;
-    cfg.qreg = nparts == 1 && cpl * batch <= (cpl >= 4 ? 4 : 2);
+    cfg.nparts = (slots + cpl - 1) / cpl;
+    cfg.qreg = cfg.nparts == 1 && cpl * batch <= (cpl >= 4 ? 4 : 2);
     return true;
   }
-  // long rows and few of them: no K split, parts instead
-  const int slots = (C + kWave - 1) / kWave;
-  int cpl = slots <= 1 ? 1 : (slots <= 2 ? 2 : 4);
-  if (cpl > max_cpl) cpl = max_cpl;
-  cfg.plog2 = 6;
-  cfg.cpl = cpl;
-  cfg.S = 1;
-  cfg.nparts = (slots + cpl - 1) / cpl;
-  cfg.qreg = false;
-  return true;
+  return false;
 }
 
 // Grid for a configuration: blocks, rows per block, and the work items every
@@ -752,9 +751,10 @@ hipError_t launch_one(const uint8_t *blob, const bqm_cq_layout &L, const LevelTa
   return hipGetLastError();
 }
 
-// Work items in flight per wave: enough to cover the wave's items (a power of
-// two), at most kRingChunks chunks (half that when a thread holds two fp32
-// activation segments).
+// Work items in flight per wave: at most two (measured: deeper rings make every
+// wave burst its loads up front, so its compute cannot start until the burst
+// has drained; two items keep 64 KB per CU in flight and let a wave compute
+// one item while the next streams), and at most kRingChunks chunks.
 template <int BATCH, int CPL, bool FUSED>
 constexpr int max_pd() {
   constexpr int kThreads = block_threads<CPL>();
@@ -767,7 +767,7 @@ hipError_t dispatch_pd(const uint8_t *blob, const bqm_cq_layout &L, const LevelT
                        const GemvArgs &A, const GemvConfig &cfg, int num_cus, hipStream_t s) {
   int blocks, rpb, items;
   grid_of<CPL>(L, cfg, num_cus, blocks, rpb, items);
-  constexpr int kMax = max_pd<BATCH, CPL, FUSED>();
+  constexpr int kMax = max_pd<BATCH, CPL, FUSED>() < 2 ? max_pd<BATCH, CPL, FUSED>() : 2;
   if (items <= 1 || kMax == 1) return launch_one<IB, BATCH, CPL, QREG, 1, FUSED>(blob, L, T, A, cfg, num_cus, s);
   if constexpr (kMax >= 2) {
     if (items <= 2 || kMax == 2) return launch_one<IB, BATCH, CPL, QREG, 2, FUSED>(blob, L, T, A, cfg, num_cus, s);
