@@ -236,6 +236,9 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
+  // the kernel addresses the weights and activations with 32-bit offsets
+  if (layout->idx_bytes >= (int64_t)1 << 30 || (int64_t)m * layout->cols >= (int64_t)1 << 30)
+    return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;
   int cus;

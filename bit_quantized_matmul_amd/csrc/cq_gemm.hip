@@ -14,16 +14,20 @@
 //    with the 1024-bias trick: fp16 bits 0x6400 | (q + 128) equal 1152 + q.
 //  * B (weights): each wave looks its own fragment up straight into registers
 //    from an LDS table indexed by an index byte (the same replicated,
-//    bank-conflict-free table as the GEMV).  Levels are bfloat16-representable
-//    and so exact in fp16; with fp16 operands the products are exact and
-//    the contraction accumulates in fp32 (v_mfma_f32_32x32x16_f16).
-//  * Per group the MFMA chain starts from zero; the group's fp32 norm is then
-//    applied per output column (acc += norm[n, g] * tile), so the norm never
-//    rounds through a 16-bit operand.
+//    bank-conflict-free table as the GEMV), and scales each fp16 level pair by
+//    the group's norm / 4 with one packed fp16 multiply.  That product is the
+//    one rounding of the path (<= 2^-11 relative per weight, ~3e-4 on y); the
+//    1/4 keeps level x norm (levels <= 2.74) inside the fp16 range for any
+//    fp16 norm.  MFMA products of fp16 operands are exact and accumulate in
+//    fp32 (v_mfma_f32_32x32x16_f16) straight through all of K: no per-group
+//    epilogue interrupts the chain.
 //  * The k order inside a group is permuted consistently for A and B: in step
 //    s (0..7) lane half h supplies columns 64h + 8s .. +8, so each lane reads
 //    one contiguous run of 64 indices per group.
-//  * Workgroup tiles are 128 (m) x 128 (n), 4 waves of 64 x 64.  Consecutive
+//  * Workgroup tiles are (64 MB) x (64 NB), four waves of (32 MB) x (32 NB),
+//    i.e. MB x NB MFMA tiles of 32 x 32 per wave.  Larger wave tiles read less
+//    LDS per flop; the launch takes the largest tile that still gives every
+//    CU work (128 x 256 for wide matrices, 128 x 128, or 64 x 128).  Consecutive
 //    tiles (the m-tiles of one n-block, which share weights) are mapped to the
 //    same XCD: hardware deals workgroups round-robin over the 8 XCDs.
 #include "bqm_common.h"
@@ -32,7 +36,6 @@ namespace bqm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128, kBN = 128;
 constexpr int kAStride = kGroup + 8;   // fp16 elements per A row in LDS (272 B: conflict-free b128 reads)
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -129,15 +132,53 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t &lo, uint32_t
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - bias);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
+constexpr int kDepth = 4;                  // groups of A and B in flight per thread
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The lane's 8*IB index bytes of one group (64 indices): whole 32-bit words.
 template <int IB>
+__device__ __forceinline__ void load_b_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[2 * IB]) {
+  if constexpr (IB == 4) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (IB == 3) {
+    const u32x3 a = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
+    const u32x3 b = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off + 12, 0, 0));
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = b.x; w[4] = b.y; w[5] = b.z;
+  } else if constexpr (IB == 2) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else {
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    w[0] = a.x; w[1] = a.y;
+  }
+}
+
+// Loads run kDepth groups ahead in registers through raw buffer loads (rows
+// past M or N read zeros), all issued unconditionally so the compiler waits
+// for exactly one group's loads at a time; groups past K read zeros too, so
+// the loop runs a whole number of kDepth rounds with no branch.
+template <int IB, int MB, int NB>
 __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     const uint8_t *__restrict__ idx, const uint16_t *__restrict__ norms,
     const int8_t *__restrict__ q, const float *__restrict__ scale, float *__restrict__ y,
-    int M, int N, int K, int tiles_m, int tiles_n, LevelTable T) {
+    int M, int N, int K, int tiles_m, int tiles_n, uint32_t idx_bytes, uint32_t norm_bytes,
+    LevelTable T) {
   constexpr int TB = table_bytes<IB>();
+  constexpr int kBM = 64 * MB, kBN = 64 * NB;
+  constexpr int kNB = NB;
+  constexpr int kTPR = kThreads / kBM;             // threads per A row
+  constexpr int kAV = kGroup / kTPR / 16;          // 16-byte A loads per thread per group
   __shared__ __align__(16) uint8_t tab[TB];
   __shared__ __align__(16) _Float16 As[2][kBM * kAStride];
-
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -152,134 +193,167 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   const int mt = tile % tiles_m, nt = tile / tiles_m;
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int ng = K / kGroup;
+  const int rounds = (ng + kDepth - 1) / kDepth;
   const int row_bytes = K * IB / 8;
   const uint32_t laneoff = (uint32_t)(lane * entry_bytes<IB>()) & 255u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)((size_t)M * K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(idx, idx_bytes);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(norms, norm_bytes);
 
   for (int o = t * 16; o < TB; o += kThreads * 16)
     *reinterpret_cast<uint4 *>(tab + o) = table_entry16<IB>(o >> 8, T);
 
-  // A tile loader: thread t converts 64 int8 of row t/2, half t%2.
-  const int arow = t >> 1, ahalf = t & 1;
+  // A: thread t holds 16 kAV int8 of row t / kTPR of a group
+  const int arow = t / kTPR, acol = (t % kTPR) * (16 * kAV);
   const bool arow_ok = (m0 + arow) < M;
-  const int8_t *aptr = q + (size_t)(m0 + (arow_ok ? arow : 0)) * K + 64 * ahalf;
-  uint4 apre[4];
-  auto load_a = [&](int g) {
+  const uint32_t abase = arow_ok ? (uint32_t)((m0 + arow) * K + acol) : kOOB;
+  // B: per n-block nb, lane holds row n = n0 + 64 wn + 32 nb + lr, indices
+  // 64 lh .. 64 lh + 63 of the group (a run of 8*IB bytes)
+  int ncol[kNB];
+  bool nok[kNB];
+  uint32_t bbase[kNB], nbase[kNB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      apre[i] = arow_ok ? *reinterpret_cast<const uint4 *>(aptr + (size_t)g * kGroup + 16 * i)
-                        : make_uint4(0, 0, 0, 0);
+  for (int nb = 0; nb < kNB; ++nb) {
+    ncol[nb] = n0 + 32 * NB * wn + 32 * nb + lr;
+    nok[nb] = ncol[nb] < N;
+    bbase[nb] = nok[nb] ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh) : kOOB;
+    nbase[nb] = nok[nb] ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
+  }
+  u32x4 apre[kDepth][kAV];
+  uint32_t bpre[kDepth][kNB][2 * IB], npre[kDepth][kNB];
+  auto issue = [&](int g, int slot) {
+    const bool gok = g < ng;
+#pragma unroll
+    for (int i = 0; i < kAV; ++i)
+      apre[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          ra, gok ? abase + (uint32_t)(g * kGroup + 16 * i) : kOOB, 0, 0));
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      load_b_words<IB>(rb, gok ? bbase[nb] + (uint32_t)(g * 16 * IB) : kOOB, bpre[slot][nb]);
+      npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(
+          rn, gok ? ((nbase[nb] + 2u * g) & ~3u) : kOOB, 0, 0);
+    }
   };
-  auto store_a = [&](int buf) {
-    _Float16 *dst = &As[buf][arow * kAStride + 64 * ahalf];
+  auto store_a = [&](int slot, int buf) {
+    _Float16 *dst = &As[buf][arow * kAStride + acol];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAV; ++i) {
       uint32_t o[8];
-      i8x4_to_f16x4(apre[i].x, o[0], o[1]);
-      i8x4_to_f16x4(apre[i].y, o[2], o[3]);
-      i8x4_to_f16x4(apre[i].z, o[4], o[5]);
-      i8x4_to_f16x4(apre[i].w, o[6], o[7]);
+      i8x4_to_f16x4(apre[slot][i].x, o[0], o[1]);
+      i8x4_to_f16x4(apre[slot][i].y, o[2], o[3]);
+      i8x4_to_f16x4(apre[slot][i].z, o[4], o[5]);
+      i8x4_to_f16x4(apre[slot][i].w, o[6], o[7]);
       *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
       *reinterpret_cast<uint4 *>(dst + 16 * i + 8) = make_uint4(o[4], o[5], o[6], o[7]);
     }
   };
 
-  // B: per n-block nb, lane holds row n = n0 + 64 wn + 32 nb + lr, indices
-  // 64 lh .. 64 lh + 63 of the current group.
-  int ncol[2];
-  bool nok[2];
+  f32x16 acc[MB][kNB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    ncol[nb] = n0 + 64 * wn + 32 * nb + lr;
-    nok[nb] = ncol[nb] < N;
-  }
-  uint32_t bw[2][2 * IB], bpre[2][2 * IB];
-  uint16_t nrm16[2], nrmpre[2];
-  auto load_b = [&](int g) {
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint8_t *p = idx + (size_t)(nok[nb] ? ncol[nb] : 0) * row_bytes +
-                         (size_t)g * 16 * IB + 8 * IB * lh;
-#pragma unroll
-      for (int i = 0; i < 2 * IB; ++i)
-        bpre[nb][i] = nok[nb] ? *reinterpret_cast<const uint32_t *>(p + 4 * i) : 0u;
-      nrmpre[nb] = nok[nb] ? norms[(size_t)ncol[nb] * ng + g] : (uint16_t)0;
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(d, d);
+  store_a(0, 0);
   __syncthreads();
 
-  for (int g = 0; g < ng; ++g) {
-    const int buf = g & 1;
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  for (int r0 = 0; r0 < rounds; ++r0) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int d = 0; d < kDepth; ++d) {
+      const int g = r0 * kDepth + d;
+      uint32_t bw[kNB][2 * IB];
+      h2v nq[kNB];
 #pragma unroll
-      for (int i = 0; i < 2 * IB; ++i) bw[nb][i] = bpre[nb][i];
-      nrm16[nb] = nrmpre[nb];
+      for (int nb = 0; nb < kNB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 2 * IB; ++i) bw[nb][i] = bpre[d][nb][i];
+        // the group's norm / 4 as an fp16 pair (scaling by 1/4 is exact)
+        const uint32_t nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + g)) & 1u) * 16u);
+        const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)0.25f;
+        nq[nb] = h2v{h, h};
+      }
+      const _Float16 *abase_l = &As[g & 1][(32 * MB * wm + lr) * kAStride + 64 * lh];
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        f16x8 a[MB], b[kNB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          a[mb] = *reinterpret_cast<const f16x8 *>(abase_l + 32 * mb * kAStride + 8 * s8);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const f16x8 lv = lookup_step<IB>(bw[nb], s8, tab, laneoff);
+          f16x8 sc;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const h2v pr = {lv[2 * p], lv[2 * p + 1]};
+            const h2v rr = pr * nq[nb];
+            sc[2 * p] = rr.x;
+            sc[2 * p + 1] = rr.y;
+          }
+          b[nb] = sc;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      }
+      issue(g + kDepth, d);                            // refill this slot, kDepth groups ahead
+      store_a((d + 1) % kDepth, (g + 1) & 1);          // A of group g + 1 into the other buffer
+      __syncthreads();
     }
-    if (g + 1 < ng) {
-      load_a(g + 1);
-      load_b(g + 1);
-    }
-    f32x16 d[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) d[i][j][r] = 0.0f;
-    const _Float16 *abase = &As[buf][(64 * wm + lr) * kAStride + 64 * lh];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      f16x8 a[2], b[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[mb] = *reinterpret_cast<const f16x8 *>(abase + 32 * mb * kAStride + 8 * s);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = lookup_step<IB>(bw[nb], s, tab, laneoff);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          d[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], d[mb][nb], 0, 0, 0);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float nv = half_bits_to_float(nrm16[nb]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][nb][r] = fmaf(nv, d[mb][nb][r], acc[mb][nb][r]);
-    }
-    if (g + 1 < ng) store_a(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: D row i = 8*(r/4) + 4*lh + (r%4), column lr
-  const float cfac = T.cscale * (1.0f / kGroup);
+  const float cfac = T.cscale * (4.0f / kGroup);     // the B operand carries norm / 4
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 64 * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int m = m0 + 32 * MB * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (m < M) {
         const float f = scale[m] * cfac;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
           if (nok[nb]) y[(size_t)m * N + ncol[nb]] = acc[mb][nb][r] * f;
       }
     }
   }
+}
+
+template <int IB, int MB, int NB>
+hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                        const int8_t *q, const float *scale, int m, float *y, hipStream_t s) {
+  const int tiles_m = (m + 64 * MB - 1) / (64 * MB);
+  const int tiles_n = (L.rows + 64 * NB - 1) / (64 * NB);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  const uint16_t *norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
+  const uint32_t ib = (uint32_t)L.idx_bytes;
+  const uint32_t nbytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);   // whole words (blob pads to 64)
+  cq_gemm_kernel<IB, MB, NB><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+                                                       tiles_m, tiles_n, ib, nbytes, T);
+  return hipGetLastError();
+}
+
+// Tile shape: the largest of 128x256, 128x128 (m x n) whose tile count still
+// covers the CUs in one round, else 64x128.
+template <int IB>
+hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                     const int8_t *q, const float *scale, int m, float *y, int num_cus,
+                     hipStream_t s) {
+  auto tiles = [&](int bm, int bn) {
+    return (long)((m + bm - 1) / bm) * ((L.rows + bn - 1) / bn);
+  };
+  if (tiles(128, 256) >= (long)num_cus * 7 / 8)
+    return launch_tiles<IB, 2, 4>(blob, L, T, q, scale, m, y, s);
+  if (tiles(128, 128) >= (long)num_cus * 7 / 8)
+    return launch_tiles<IB, 2, 2>(blob, L, T, q, scale, m, y, s);
+  return launch_tiles<IB, 1, 2>(blob, L, T, q, scale, m, y, s);
 }
 
 }  // namespace
@@ -287,27 +361,12 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
 hipError_t launch_cq_gemm(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                           const int8_t *q, const float *scale, int m, float *y, int num_cus,
                           hipStream_t s) {
-  (void)num_cus;
-  const int tiles_m = (m + kBM - 1) / kBM;
-  const int tiles_n = (L.rows + kBN - 1) / kBN;
-  const int ntiles = tiles_m * tiles_n;
-  const int grid = ((ntiles + 7) / 8) * 8;
-  const uint16_t *norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
   switch (L.index_bits) {
-    case 1:
-      cq_gemm_kernel<1><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols, tiles_m, tiles_n, T);
-      break;
-    case 2:
-      cq_gemm_kernel<2><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols, tiles_m, tiles_n, T);
-      break;
-    case 3:
-      cq_gemm_kernel<3><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols, tiles_m, tiles_n, T);
-      break;
-    default:
-      cq_gemm_kernel<4><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols, tiles_m, tiles_n, T);
-      break;
+    case 1: return launch_ib<1>(blob, L, T, q, scale, m, y, num_cus, s);
+    case 2: return launch_ib<2>(blob, L, T, q, scale, m, y, num_cus, s);
+    case 3: return launch_ib<3>(blob, L, T, q, scale, m, y, num_cus, s);
+    default: return launch_ib<4>(blob, L, T, q, scale, m, y, num_cus, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace bqm

@@ -118,10 +118,12 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
 /* Prefill GEMM on packed CQ weights (Needle article, section 3: prefill is a
  * GEMM with the same layout, every row one reduction stream).  Same sum as
  * cq_gemv for m tokens: q [device] int8 [m, cols], scale [device] fp32 [m],
- * y [device] fp32 [m, rows].  The weight tile is dequantized to bfloat16
- * codebook values (exact: the codebook is bfloat16-representable) and
- * multiplied on the matrix cores with fp32 accumulation; the group norm and
- * token scale are applied in fp32.  m >= 1, group must be 128. */
+ * y [device] fp32 [m, rows].  The weight tile is the codebook level times
+ * the group norm, rounded once to fp16 (relative error <= 2^-11 per weight);
+ * activations enter as exact fp16 integers; the matrix cores accumulate in
+ * fp32 and the token scale is applied in fp32.  m >= 1, group must be 128.
+ * Returns BQM_ENOTSUP when the packed indices or m * cols exceed 2^30 bytes
+ * (the kernel addresses them with 32-bit offsets). */
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int m, float *y, bqm_stream_t stream);
 

@@ -240,17 +240,20 @@ def test_full_size_decode_gemv_sampled(rows, cols, codebooks):
     assert omm.rel_l2(y[:, sel], ref) <= TOL
 
 
-@pytest.mark.parametrize("rows", [14336, 4096])
-def test_full_size_prefill_gemm_sampled(rows, codebooks):
-    rng = np.random.default_rng(900 + rows)
-    m, cols = inputs.PREFILL_TOKENS, 4096
+# the prefill shapes (512 tokens, K = 4096), plus shapes that select each
+# GEMM tile (128x256 for 14336 / 14200 outputs, 128x128 for 7168 and for the
+# ragged 300 x 14000, 64x128 for 4096), with ragged tiles in m and n
+@pytest.mark.parametrize("m,rows", [(512, 14336), (512, 4096), (512, 7168), (300, 14000), (512, 14200)])
+def test_full_size_prefill_gemm_sampled(m, rows, codebooks):
+    rng = np.random.default_rng(900 + rows + m)
+    cols = 4096
     w = inputs.weight_matrix(rng, rows, cols)
     x = inputs.activations(rng, m, cols)
     lay = B.cq_pack_info(rows, cols, 128, 4)
     blob = B.cq_pack(dev(w), lay, codebooks[4])
     q, s = B.act_fwht_quant_a8(dev(x))
     y = host(B.cq_gemm(blob, lay, codebooks[4], q, s))
-    sel = sampled_rows(rng, rows, 40)
+    sel = np.unique(np.concatenate([sampled_rows(rng, rows, 40), np.arange(rows - 3, rows)]))
     idx, n16 = ocq.split_blob(host(blob), rows, cols, 128, 4)
     ref = omm.cq_reference(idx[sel], n16[sel], 128, 4, codebooks[4], host(q), host(s))
     assert omm.rel_l2(y[:, sel], ref) <= TOL
