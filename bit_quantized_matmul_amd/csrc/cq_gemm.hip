@@ -177,8 +177,11 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   constexpr int kNB = NB;
   constexpr int kTPR = kThreads / kBM;             // threads per A row
   constexpr int kAV = kGroup / kTPR / 16;          // 16-byte A loads per thread per group
-  __shared__ __align__(16) uint8_t tab[TB];
-  __shared__ __align__(16) _Float16 As[2][kBM * kAStride];
+  // one LDS array with the level table at offset 0, so a lookup address is
+  // the v_perm result itself (no base add per lookup), then the A buffers
+  __shared__ __align__(16) uint8_t smem[TB + 2 * kBM * kAStride * 2];
+  uint8_t *const tab = smem;
+  _Float16 (*As)[kBM * kAStride] = reinterpret_cast<_Float16 (*)[kBM * kAStride]>(smem + TB);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
