@@ -24,18 +24,24 @@
 //  * The k order inside a group is permuted consistently for A and B: in step
 //    s (0..7) lane half h supplies columns 64h + 8s .. +8, so each lane reads
 //    one contiguous run of 64 indices per group.
-//  * Workgroup tiles are (64 MB) x (64 NB), four waves of (32 MB) x (32 NB),
-//    i.e. MB x NB MFMA tiles of 32 x 32 per wave.  Larger wave tiles read less
-//    LDS per flop; the launch takes the largest tile that still gives every
-//    CU work (128 x 256 for wide matrices, 128 x 128, or 64 x 128).  Consecutive
-//    tiles (the m-tiles of one n-block, which share weights) are mapped to the
-//    same XCD: hardware deals workgroups round-robin over the 8 XCDs.
+//  * Eight waves per workgroup, two per SIMD, so one wave's LDS and barrier
+//    waits overlap the other's MFMAs.  Waves 0-3 take steps 0-3 of every
+//    group and waves 4-7 steps 4-7 (a split of K inside the workgroup, summed
+//    once at the end through LDS); within a half the four waves form a
+//    WM x (4 / WM) grid of MB x NB MFMA tiles of 32 x 32 each.  A wave's LDS
+//    reads per step are MB A fragments and NB level lookups, and its VALU
+//    work (address perms, norm multiplies) scales with NB alone, so the wide
+//    tile uses tall waves (128 x 64 each).  The launch takes the largest
+//    workgroup tile that still gives every CU work (128 x 256 for wide
+//    matrices, 128 x 128, or 64 x 128).  Consecutive tiles (the m-tiles of one
+//    n-block, which share weights) are mapped to the same XCD: hardware deals
+//    workgroups round-robin over the 8 XCDs.
 #include "bqm_common.h"
 
 namespace bqm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                 // 8 waves: two per SIMD
 constexpr int kAStride = kGroup + 8;   // fp16 elements per A row in LDS (272 B: conflict-free b128 reads)
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -69,12 +75,10 @@ __device__ __forceinline__ uint32_t perm_addr(uint32_t w, uint32_t laneoff) {
   return __builtin_amdgcn_perm(w, laneoff, 0x0C0C0000u | ((4u + K) << 8));
 }
 
-// Bytes of indices a lane holds per group: 64 indices.
-template <int IB> constexpr int lane_words() { return 2 * IB; }   // 8*IB bytes
-
-// B operand for step s: the 8 levels of indices 8s..8s+7 of the lane's 64.
+// B operand for step s (0..3) of a lane's half group: the 8 levels of indices
+// 8s .. 8s+7 of its 32, whose codes sit in IB words (4*IB bytes).
 template <int IB>
-__device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[2 * IB], int s,
+__device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[IB], int s,
                                              const uint8_t *tab, uint32_t laneoff) {
   uint32_t r[4];
   if constexpr (IB == 4) {           // one dword = 8 indices = 4 pair lookups
@@ -95,7 +99,7 @@ __device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[2 * IB], int s
     }
     r[0] = e0.x; r[1] = e0.y; r[2] = e1.x; r[3] = e1.y;
   } else if constexpr (IB == 1) {    // one byte -> one 8-level entry
-    const uint32_t w = wd[s >> 2];
+    const uint32_t w = wd[0];
     uint4 e;
     switch (s & 3) {
       case 0: e = *reinterpret_cast<const uint4 *>(tab + perm_addr<0>(w, laneoff)); break;
@@ -108,7 +112,7 @@ __device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[2 * IB], int s
     const int bit = 24 * s;          // bit offset of the step's 8 indices
     const int wi = bit >> 5, sh = bit & 31;
     const uint32_t lo = wd[wi];
-    const uint32_t hi = (wi + 1 < 2 * IB) ? wd[wi + 1] : 0u;
+    const uint32_t hi = (wi + 1 < IB) ? wd[wi + 1] : 0u;
     const uint32_t v = __builtin_amdgcn_alignbit(hi, lo, sh);   // bits [bit, bit+32)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -136,29 +140,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
-constexpr int kDepth = 4;                  // groups of A and B in flight per thread
+constexpr int kDepth = 3;                  // groups of A and B in flight per thread
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// The lane's 8*IB index bytes of one group (64 indices): whole 32-bit words.
+// The lane's 4*IB index bytes of one half group (32 indices): IB whole words.
 template <int IB>
-__device__ __forceinline__ void load_b_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[2 * IB]) {
+__device__ __forceinline__ void load_b_half(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[IB]) {
   if constexpr (IB == 4) {
     const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
   } else if constexpr (IB == 3) {
     const u32x3 a = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
-    const u32x3 b = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off + 12, 0, 0));
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = b.x; w[4] = b.y; w[5] = b.z;
+    w[0] = a.x; w[1] = a.y; w[2] = a.z;
   } else if constexpr (IB == 2) {
-    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  } else {
     const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
     w[0] = a.x; w[1] = a.y;
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
 }
 
@@ -166,26 +167,30 @@ __device__ __forceinline__ void load_b_words(__amdgpu_buffer_rsrc_t r, uint32_t 
 // past M or N read zeros), all issued unconditionally so the compiler waits
 // for exactly one group's loads at a time; groups past K read zeros too, so
 // the loop runs a whole number of kDepth rounds with no branch.
-template <int IB, int MB, int NB>
+template <int IB, int WM, int MB, int NB>
 __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     const uint8_t *__restrict__ idx, const uint16_t *__restrict__ norms,
     const int8_t *__restrict__ q, const float *__restrict__ scale, float *__restrict__ y,
     int M, int N, int K, int tiles_m, int tiles_n, uint32_t idx_bytes, uint32_t norm_bytes,
     LevelTable T) {
   constexpr int TB = table_bytes<IB>();
-  constexpr int kBM = 64 * MB, kBN = 64 * NB;
-  constexpr int kNB = NB;
-  constexpr int kTPR = kThreads / kBM;             // threads per A row
-  constexpr int kAV = kGroup / kTPR / 16;          // 16-byte A loads per thread per group
-  // one LDS array with the level table at offset 0, so a lookup address is
-  // the v_perm result itself (no base add per lookup), then the A buffers
-  __shared__ __align__(16) uint8_t smem[TB + 2 * kBM * kAStride * 2];
+  constexpr int WN = 4 / WM;
+  constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * WN;
+  constexpr int kAV = kBM / 64;                    // 16-byte A loads per thread per group
+  constexpr int kYS = kBN + 8;                     // epilogue tile row stride (floats): rows 4 apart sit 32 banks apart
+  constexpr int kLoopBytes = TB + 2 * kBM * kAStride * 2, kYBytes = kBM * kYS * 4;
+  static_assert(kThreads == 512 && kGroup == 128 && kAV >= 1, "A staging: 8 lanes per 128-byte row slice, 64 rows a pass");
+  // One LDS array: the level table at offset 0 (a lookup address is the
+  // v_perm result itself, no base add) and two A buffers; the epilogue then
+  // reuses it for the fp32 output tile.
+  __shared__ __align__(16) uint8_t smem[kLoopBytes > kYBytes ? kLoopBytes : kYBytes];
   uint8_t *const tab = smem;
   _Float16 (*As)[kBM * kAStride] = reinterpret_cast<_Float16 (*)[kBM * kAStride]>(smem + TB);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int kh = wave >> 2;                        // which half of each group's 8 steps
+  const int wm = (wave & 3) / WN, wn = (wave & 3) % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
   // XCD-aware tile order: tiles xcd*per .. xcd*per+per-1 run on one XCD
@@ -206,139 +211,221 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   for (int o = t * 16; o < TB; o += kThreads * 16)
     *reinterpret_cast<uint4 *>(tab + o) = table_entry16<IB>(o >> 8, T);
 
-  // A: thread t holds 16 kAV int8 of row t / kTPR of a group
-  const int arow = t / kTPR, acol = (t % kTPR) * (16 * kAV);
-  const bool arow_ok = (m0 + arow) < M;
-  const uint32_t abase = arow_ok ? (uint32_t)((m0 + arow) * K + acol) : kOOB;
-  // B: per n-block nb, lane holds row n = n0 + 64 wn + 32 nb + lr, indices
-  // 64 lh .. 64 lh + 63 of the group (a run of 8*IB bytes)
-  int ncol[kNB];
-  bool nok[kNB];
-  uint32_t bbase[kNB], nbase[kNB];
+  // A: load i of thread t is 16 int8 of row t / 8 + 64 i at bytes 16 (t % 8) of
+  // the group, so eight lanes read one row's whole 128-byte slice
+  const int arow0 = t >> 3, acol = (t & 7) * 16;
+  uint32_t abase[kAV];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    ncol[nb] = n0 + 32 * NB * wn + 32 * nb + lr;
-    nok[nb] = ncol[nb] < N;
-    bbase[nb] = nok[nb] ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh) : kOOB;
-    nbase[nb] = nok[nb] ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
+  for (int i = 0; i < kAV; ++i) {
+    const int r = m0 + arow0 + 64 * i;
+    abase[i] = r < M ? (uint32_t)(r * K + acol) : kOOB;
   }
+  // B: per n-block nb, lane holds row n = n0 + 32 NB wn + 32 nb + lr; of the
+  // group's 8*IB-byte run of indices 64 lh .. 64 lh + 63 it loads the half its
+  // steps use (4*IB bytes)
+  int ncol[NB];
+  uint32_t bbase[NB], nbase[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    ncol[nb] = n0 + 32 * NB * wn + 32 * nb + lr;
+    const bool ok = ncol[nb] < N;
+    bbase[nb] = ok ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh + 4 * IB * kh) : kOOB;
+    nbase[nb] = ok ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
+  }
+  // Each tile walks the groups from its own starting point (wrapping), so the
+  // tiles that share A rows or weight rows read different k-slices at any one
+  // time instead of all hitting the same memory channels together.
+  const int rot = (nt * 7 + mt * 3) % ng;
+  auto kgroup = [&](int g) { const int x = g + rot; return x < ng ? x : x - ng; };
   u32x4 apre[kDepth][kAV];
-  uint32_t bpre[kDepth][kNB][2 * IB], npre[kDepth][kNB];
+  uint32_t bpre[kDepth][NB][IB], npre[kDepth][NB];
   auto issue = [&](int g, int slot) {
     const bool gok = g < ng;
+    const int gg = kgroup(g);
 #pragma unroll
     for (int i = 0; i < kAV; ++i)
       apre[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          ra, gok ? abase + (uint32_t)(g * kGroup + 16 * i) : kOOB, 0, 0));
+          ra, gok ? abase[i] + (uint32_t)(gg * kGroup) : kOOB, 0, 0));
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      load_b_words<IB>(rb, gok ? bbase[nb] + (uint32_t)(g * 16 * IB) : kOOB, bpre[slot][nb]);
+    for (int nb = 0; nb < NB; ++nb) {
+      load_b_half<IB>(rb, gok ? bbase[nb] + (uint32_t)(gg * 16 * IB) : kOOB, bpre[slot][nb]);
       npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(
-          rn, gok ? ((nbase[nb] + 2u * g) & ~3u) : kOOB, 0, 0);
+          rn, gok ? ((nbase[nb] + 2u * gg) & ~3u) : kOOB, 0, 0);
     }
   };
-  auto store_a = [&](int slot, int buf) {
-    _Float16 *dst = &As[buf][arow * kAStride + acol];
-#pragma unroll
-    for (int i = 0; i < kAV; ++i) {
-      uint32_t o[8];
-      i8x4_to_f16x4(apre[slot][i].x, o[0], o[1]);
-      i8x4_to_f16x4(apre[slot][i].y, o[2], o[3]);
-      i8x4_to_f16x4(apre[slot][i].z, o[4], o[5]);
-      i8x4_to_f16x4(apre[slot][i].w, o[6], o[7]);
-      *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4 *>(dst + 16 * i + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
+  // one 16-byte A load (16 int8) -> 16 fp16 in LDS buffer buf
+  auto store_a_part = [&](int slot, int buf, int i) {
+    _Float16 *dst = &As[buf][(arow0 + 64 * i) * kAStride + acol];
+    uint32_t o[8];
+    i8x4_to_f16x4(apre[slot][i].x, o[0], o[1]);
+    i8x4_to_f16x4(apre[slot][i].y, o[2], o[3]);
+    i8x4_to_f16x4(apre[slot][i].z, o[4], o[5]);
+    i8x4_to_f16x4(apre[slot][i].w, o[6], o[7]);
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   };
 
-  f32x16 acc[MB][kNB];
+  f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNB; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(d, d);
-  store_a(0, 0);
+#pragma unroll
+  for (int i = 0; i < kAV; ++i) store_a_part(0, 0, i);
   __syncthreads();
 
   typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  // A wave's half group runs as 4 steps x MB chunks; chunk (s, mb) is the NB
+  // MFMAs of m-block mb at step s.  Around them the wave issues the work of
+  // later chunks, in a fixed order that the scheduling barriers keep: the A
+  // fragment two chunks ahead, the next step's level lookups (at mb 0) and
+  // norm multiplies (at the last mb), a part of the next group's A staging.
+  // The last step looks up the next group's first step (the table never
+  // changes); the workgroup barrier sits in the last chunk, where every wave
+  // has written its part of the next group's A and read its last fragment of
+  // this group's, followed by the next group's first A reads.
+  constexpr int kChunks = 4 * MB;
+  uint32_t bw[NB][IB];
+  h2v nq[NB];
+  f16x8 lvr[NB], bfr[2][NB], ar[3];
+  auto scale_b = [&](const f16x8 &lv, h2v f) {
+    f16x8 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const h2v rr = h2v{lv[2 * p], lv[2 * p + 1]} * f;
+      o[2 * p] = rr.x;
+      o[2 * p + 1] = rr.y;
+    }
+    return o;
+  };
+  // group g's index words and norm / 4 as an fp16 pair (scaling by 1/4 is exact)
+  auto take_group = [&](int g, int d) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < IB; ++i) bw[nb][i] = bpre[d][nb][i];
+      const uint32_t nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
+      const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)0.25f;
+      nq[nb] = h2v{h, h};
+    }
+  };
+  // lane's A fragment for chunk c: rows 32 (MB wm + mb) + lr, step 4 kh + s
+  const int afrag = (32 * MB * wm + lr) * kAStride + 64 * lh + 32 * kh;
+  auto read_a = [&](int buf, int c) {
+    return *reinterpret_cast<const f16x8 *>(&As[buf][afrag + 32 * (c % MB) * kAStride + 8 * (c / MB)]);
+  };
+  take_group(0, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bw[nb], 0, tab, laneoff);
+  ar[0] = read_a(0, 0);
+  if (kChunks > 1) ar[1] = read_a(0, 1);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) bfr[0][nb] = scale_b(lvr[nb], nq[nb]);
+  __builtin_amdgcn_sched_barrier(0);
   for (int r0 = 0; r0 < rounds; ++r0) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int g = r0 * kDepth + d;
-      uint32_t bw[kNB][2 * IB];
-      h2v nq[kNB];
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
+      for (int c = 0; c < kChunks; ++c) {
+        const int s = c / MB, mb = c % MB;
 #pragma unroll
-        for (int i = 0; i < 2 * IB; ++i) bw[nb][i] = bpre[d][nb][i];
-        // the group's norm / 4 as an fp16 pair (scaling by 1/4 is exact)
-        const uint32_t nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + g)) & 1u) * 16u);
-        const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)0.25f;
-        nq[nb] = h2v{h, h};
-      }
-      const _Float16 *abase_l = &As[g & 1][(32 * MB * wm + lr) * kAStride + 64 * lh];
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ar[c % 3], bfr[s & 1][nb], acc[mb][nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (mb == 0) {
+          if (s == 3) take_group(g + 1, (d + 1) % kDepth);
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        f16x8 a[MB], b[kNB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          a[mb] = *reinterpret_cast<const f16x8 *>(abase_l + 32 * mb * kAStride + 8 * s8);
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const f16x8 lv = lookup_step<IB>(bw[nb], s8, tab, laneoff);
-          f16x8 sc;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const h2v pr = {lv[2 * p], lv[2 * p + 1]};
-            const h2v rr = pr * nq[nb];
-            sc[2 * p] = rr.x;
-            sc[2 * p + 1] = rr.y;
-          }
-          b[nb] = sc;
+          for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bw[nb], (s + 1) & 3, tab, laneoff);
         }
+        if (c + 2 < kChunks) ar[(c + 2) % 3] = read_a(g & 1, c + 2);
+        if (c >= 1 && c <= kAV) store_a_part((d + 1) % kDepth, (g + 1) & 1, c - 1);   // A of group g + 1
+        if (mb == MB - 1) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+          for (int nb = 0; nb < NB; ++nb) bfr[(s + 1) & 1][nb] = scale_b(lvr[nb], nq[nb]);
+        }
+        if (c == kChunks - 1) {
+          issue(g + kDepth, d);                    // refill this slot, kDepth groups ahead
+          __syncthreads();
+          ar[0] = read_a((g + 1) & 1, 0);
+          if (kChunks > 1) ar[1] = read_a((g + 1) & 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      issue(g + kDepth, d);                            // refill this slot, kDepth groups ahead
-      store_a((d + 1) % kDepth, (g + 1) & 1);          // A of group g + 1 into the other buffer
-      __syncthreads();
     }
   }
 
-  // epilogue: D row i = 8*(r/4) + 4*lh + (r%4), column lr
+  // Epilogue through LDS (free now).  The two k-halves meet there: waves 4-7
+  // park their accumulators as an fp32 tile, waves 0-3 add theirs in place,
+  // then each row leaves as whole 16-byte chunks, so one store instruction
+  // writes a run of contiguous bytes.  MFMA D layout: register r of a lane
+  // holds row 8 (r / 4) + 4 lh + r % 4, column lr of its 32 x 32 tile.
+  float *const ys = reinterpret_cast<float *>(smem);
+  auto ypos = [&](int mb, int nb, int r) {
+    return (32 * MB * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3)) * kYS + 32 * NB * wn + 32 * nb + lr;
+  };
+  __syncthreads();                                 // every wave is done with the table and A buffers
+  if (kh == 1) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ys[ypos(mb, nb, r)] = acc[mb][nb][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = ypos(mb, nb, r);
+          ys[p] = acc[mb][nb][r] + ys[p];
+        }
+  }
+  __syncthreads();
   const float cfac = T.cscale * (4.0f / kGroup);     // the B operand carries norm / 4
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 32 * MB * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (m < M) {
-        const float f = scale[m] * cfac;
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          if (nok[nb]) y[(size_t)m * N + ncol[nb]] = acc[mb][nb][r] * f;
-      }
+  constexpr int kLPR = kBN / 4;                    // threads per tile row, 4 columns each
+  constexpr int kRPP = kThreads / kLPR;            // rows per pass
+  const int cr = t / kLPR, cc = (t % kLPR) * 4;
+  const int n = n0 + cc;
+  const bool vec = ((N & 3) == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+#pragma unroll 4
+  for (int p = 0; p < kBM / kRPP; ++p) {
+    const int row = p * kRPP + cr, m = m0 + row;
+    if (m >= M) continue;
+    const float f = scale[m] * cfac;
+    const float4 v = *reinterpret_cast<const float4 *>(&ys[row * kYS + cc]);
+    float *dst = y + (size_t)m * N + n;
+    if (vec && n + 3 < N) {
+      *reinterpret_cast<float4 *>(dst) = make_float4(v.x * f, v.y * f, v.z * f, v.w * f);
+    } else {
+      if (n < N) dst[0] = v.x * f;
+      if (n + 1 < N) dst[1] = v.y * f;
+      if (n + 2 < N) dst[2] = v.z * f;
+      if (n + 3 < N) dst[3] = v.w * f;
     }
   }
 }
 
-template <int IB, int MB, int NB>
+template <int IB, int WM, int MB, int NB>
 hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                         const int8_t *q, const float *scale, int m, float *y, hipStream_t s) {
-  const int tiles_m = (m + 64 * MB - 1) / (64 * MB);
-  const int tiles_n = (L.rows + 64 * NB - 1) / (64 * NB);
+  constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * (4 / WM);
+  const int tiles_m = (m + kBM - 1) / kBM;
+  const int tiles_n = (L.rows + kBN - 1) / kBN;
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
   const uint16_t *norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
   const uint32_t ib = (uint32_t)L.idx_bytes;
   const uint32_t nbytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);   // whole words (blob pads to 64)
-  cq_gemm_kernel<IB, MB, NB><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+  cq_gemm_kernel<IB, WM, MB, NB><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
                                                        tiles_m, tiles_n, ib, nbytes, T);
   return hipGetLastError();
 }
@@ -353,10 +440,10 @@ hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTab
     return (long)((m + bm - 1) / bm) * ((L.rows + bn - 1) / bn);
   };
   if (tiles(128, 256) >= (long)num_cus * 7 / 8)
-    return launch_tiles<IB, 2, 4>(blob, L, T, q, scale, m, y, s);
+    return launch_tiles<IB, 1, 4, 2>(blob, L, T, q, scale, m, y, s);
   if (tiles(128, 128) >= (long)num_cus * 7 / 8)
-    return launch_tiles<IB, 2, 2>(blob, L, T, q, scale, m, y, s);
-  return launch_tiles<IB, 1, 2>(blob, L, T, q, scale, m, y, s);
+    return launch_tiles<IB, 2, 2, 2>(blob, L, T, q, scale, m, y, s);
+  return launch_tiles<IB, 2, 1, 2>(blob, L, T, q, scale, m, y, s);
 }
 
 }  // namespace
