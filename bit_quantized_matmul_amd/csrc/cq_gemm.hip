@@ -236,21 +236,22 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // tiles that share A rows or weight rows read different k-slices at any one
   // time instead of all hitting the same memory channels together.
   const int rot = (nt * 7 + mt * 3) % ng;
-  auto kgroup = [&](int g) { const int x = g + rot; return x < ng ? x : x - ng; };
+  // Loop steps past the last group (the loop runs whole rounds of kDepth)
+  // reload group 0 with a zero norm scale, so they add exact zeros and every
+  // load stays unconditional (no branch, no early vmcnt drain).
+  auto kgroup = [&](int g) { const int x = g + rot; return g >= ng ? 0 : (x < ng ? x : x - ng); };
   u32x4 apre[kDepth][kAV];
   uint32_t bpre[kDepth][NB][IB], npre[kDepth][NB];
   auto issue = [&](int g, int slot) {
-    const bool gok = g < ng;
     const int gg = kgroup(g);
 #pragma unroll
     for (int i = 0; i < kAV; ++i)
       apre[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          ra, gok ? abase[i] + (uint32_t)(gg * kGroup) : kOOB, 0, 0));
+          ra, abase[i] + (uint32_t)(gg * kGroup), 0, 0));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      load_b_half<IB>(rb, gok ? bbase[nb] + (uint32_t)(gg * 16 * IB) : kOOB, bpre[slot][nb]);
-      npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(
-          rn, gok ? ((nbase[nb] + 2u * gg) & ~3u) : kOOB, 0, 0);
+      load_b_half<IB>(rb, bbase[nb] + (uint32_t)(gg * 16 * IB), bpre[slot][nb]);
+      npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(rn, (nbase[nb] + 2u * gg) & ~3u, 0, 0);
     }
   };
   // one 16-byte A load (16 int8) -> 16 fp16 in LDS buffer buf
@@ -290,7 +291,6 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // has written its part of the next group's A and read its last fragment of
   // this group's, followed by the next group's first A reads.
   constexpr int kChunks = 4 * MB;
-  uint32_t bw[NB][IB];
   h2v nq[NB];
   f16x8 lvr[NB], bfr[2][NB], ar[3];
   auto scale_b = [&](const f16x8 &lv, h2v f) {
@@ -303,14 +303,13 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     }
     return o;
   };
-  // group g's index words and norm / 4 as an fp16 pair (scaling by 1/4 is exact)
+  // group g's norm / 4 as an fp16 pair (scaling by 1/4 is exact); its index
+  // words are read in place from prefetch slot d
   auto take_group = [&](int g, int d) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < IB; ++i) bw[nb][i] = bpre[d][nb][i];
       const uint32_t nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
-      const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)0.25f;
+      const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)(g < ng ? 0.25f : 0.0f);
       nq[nb] = h2v{h, h};
     }
   };
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   };
   take_group(0, 0);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bw[nb], 0, tab, laneoff);
+  for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[0][nb], 0, tab, laneoff);
   ar[0] = read_a(0, 0);
   if (kChunks > 1) ar[1] = read_a(0, 1);
 #pragma unroll
@@ -339,9 +338,10 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ar[c % 3], bfr[s & 1][nb], acc[mb][nb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (mb == 0) {
-          if (s == 3) take_group(g + 1, (d + 1) % kDepth);
+          const int sl = s == 3 ? (d + 1) % kDepth : d;   // the last step looks up the next group
+          if (s == 3) take_group(g + 1, sl);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bw[nb], (s + 1) & 3, tab, laneoff);
+          for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[sl][nb], (s + 1) & 3, tab, laneoff);
         }
         if (c + 2 < kChunks) ar[(c + 2) % 3] = read_a(g & 1, c + 2);
         if (c >= 1 && c <= kAV) store_a_part((d + 1) % kDepth, (g + 1) & 1, c - 1);   // A of group g + 1
