@@ -8,11 +8,14 @@
 //  ceil(cols/32) whole blocks and the GEMV inner loop has a fixed length 32.
 //
 // GEMV: y[b, r] = sum_blk fp32(d[r, blk]) * sum_{j<32} (nib[r, blk, j] - 8) * x[b, 32 blk + j],
-// columns >= cols are padding (weight 0) and x is never read there.
-// A workgroup takes whole rows: `P` threads share a row (one or more blocks
-// each), partial sums meet in LDS and one thread per row adds them in a fixed
-// order (deterministic).  An 18-byte block is fetched with one 16-byte load
-// from the 4-byte-aligned address below it plus one 4-byte load, then
+// columns >= cols are padding (weight 0) and x is taken as 0 there.
+// Decode matrices are small (a few hundred KB), so the kernel is built for
+// latency: P = 4..64 lanes of one wave share a row, one 18-byte block each per
+// P-block column chunk; every lane issues its weight loads before anything
+// else, the workgroup stages the chunk of x in LDS meanwhile, and the row sum
+// closes with a butterfly across the P lanes (no LDS, no second barrier).
+// An 18-byte block is fetched as the 16 bytes from the 4-byte-aligned address
+// below it plus the next 4 (2 for a final block that ends there), then
 // realigned with v_alignbyte.
 #include "bqm_common.h"
 
@@ -22,109 +25,120 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlock = 32;
 constexpr int kBlockBytes = 18;
+constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
 
 // Byte K of v as a float; matches v_cvt_f32_ubyteK.
 template <int K>
 __device__ __forceinline__ float ubyte_f(uint32_t v) { return (float)((v >> (8 * K)) & 0xFFu); }
 
-struct Q4Block {
-  float d;
-  uint32_t nib[4];   // 16 code bytes: byte k of nib[w] holds elements 8w+2k (low), 8w+2k+1 (high)
-};
-
-__device__ __forceinline__ Q4Block load_block(const uint8_t *base, size_t off, size_t total) {
-  const size_t a4 = off & ~(size_t)3;
-  const uint32_t sh = (uint32_t)(off & 3);        // 0 or 2: blocks are 2-byte aligned
-  const uint4 v = *reinterpret_cast<const uint4 *>(base + a4);
-  uint32_t v4;
-  if (a4 + 20 <= total)
-    v4 = *reinterpret_cast<const uint32_t *>(base + a4 + 16);
-  else
-    v4 = (uint32_t)*reinterpret_cast<const uint16_t *>(base + a4 + 16);
-  uint32_t w0, w1, w2, w3, w4;
-  if (sh == 0) {
-    w0 = v.x; w1 = v.y; w2 = v.z; w3 = v.w; w4 = v4;
-  } else {
-    w0 = __builtin_amdgcn_alignbyte(v.y, v.x, 2);
-    w1 = __builtin_amdgcn_alignbyte(v.z, v.y, 2);
-    w2 = __builtin_amdgcn_alignbyte(v.w, v.z, 2);
-    w3 = __builtin_amdgcn_alignbyte(v4, v.w, 2);
-    w4 = v4 >> 16;
-  }
-  Q4Block b;
-  b.d = half_bits_to_float((uint16_t)(w0 & 0xFFFFu));
-  b.nib[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
-  b.nib[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
-  b.nib[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
-  b.nib[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
-  return b;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int BATCH>
+template <int BATCH, int P>
 __global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
-    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, size_t total,
-    const float *__restrict__ x, float *__restrict__ y, int P, int R, int bpt) {
-  __shared__ float part[BATCH][kThreads];
+    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t total,
+    const float *__restrict__ x, float *__restrict__ y) {
+  constexpr int RPW = kThreads / P;        // rows per workgroup
+  constexpr int kChunk = P;                // blocks per column chunk: one per lane
+  __shared__ __align__(16) float xs[BATCH][kChunk * kBlock];
   const int t = threadIdx.x;
-  const int rl = t / P;
-  const int j = t - rl * P;
-  const bool vec_x = (cols & 3) == 0;
-  for (int base = blockIdx.x * R; base < rows; base += gridDim.x * R) {
-    const int row = base + rl;
-    const bool ok = rl < R && row < rows;
-    float acc[BATCH];
+  const int j = t % P;
+  const int row = blockIdx.x * RPW + t / P;
+  const bool rok = row < rows;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(blocks, total);
+  const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  float acc[BATCH];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) acc[b] = 0.0f;
-    if (ok) {
-      for (int i = 0; i < bpt; ++i) {
-        const int blk = j + P * i;
-        if (blk >= nblk) break;
-        const Q4Block qb = load_block(blocks, ((size_t)row * nblk + blk) * kBlockBytes, total);
-        const int c0 = blk * kBlock;
-        const int nvalid = min(kBlock, cols - c0);
+  for (int b = 0; b < BATCH; ++b) acc[b] = 0.0f;
+  for (int c0 = 0; c0 < nblk; c0 += kChunk) {
+    // the lane's block c0 + j: its loads first (out of range reads 0)
+    uint4 v[1];
+    uint32_t v4[1], sh[1];
+    {
+      const int i = 0;
+      const int blk = c0 + j;
+      const bool ok = rok && blk < nblk;
+      const uint32_t off = ok ? (uint32_t)(((size_t)row * nblk + blk) * kBlockBytes) : 0u;
+      const uint32_t a4 = off & ~3u;
+      sh[i] = off & 3u;                                    // 0 or 2: blocks are 2-byte aligned
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? a4 : kOOB, 0, 0));
+      const bool w4 = ok && a4 + 20 <= total;              // the 4 bytes after exist
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rw, w4 ? a4 + 16 : kOOB, 0, 0);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (ok && !w4) ? a4 + 16 : kOOB, 0, 0);
+      v4[i] = lo | hi;
+    }
+    // x columns [32 c0, 32 (c0 + P)) to LDS, zero past cols
+    const int col0 = c0 * kBlock;
+    const int ncol = min(kChunk * kBlock, cols - col0);
+    if (c0 > 0) __syncthreads();                           // the previous chunk's reads are done
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-          const float *xb = x + (size_t)b * cols + c0;
-          float s = 0.0f;
-          if (nvalid == kBlock && vec_x) {
+    for (int b = 0; b < BATCH; ++b) {
+      const float *xb = x + (size_t)b * cols + col0;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float4 xa = *reinterpret_cast<const float4 *>(xb + 8 * w);
-              const float4 xc = *reinterpret_cast<const float4 *>(xb + 8 * w + 4);
-              const uint32_t lo = qb.nib[w] & 0x0F0F0F0Fu;
-              const uint32_t hi = (qb.nib[w] >> 4) & 0x0F0F0F0Fu;
-              s = fmaf(ubyte_f<0>(lo) - 8.0f, xa.x, s);
-              s = fmaf(ubyte_f<0>(hi) - 8.0f, xa.y, s);
-              s = fmaf(ubyte_f<1>(lo) - 8.0f, xa.z, s);
-              s = fmaf(ubyte_f<1>(hi) - 8.0f, xa.w, s);
-              s = fmaf(ubyte_f<2>(lo) - 8.0f, xc.x, s);
-              s = fmaf(ubyte_f<2>(hi) - 8.0f, xc.y, s);
-              s = fmaf(ubyte_f<3>(lo) - 8.0f, xc.z, s);
-              s = fmaf(ubyte_f<3>(hi) - 8.0f, xc.w, s);
-            }
-          } else {
-            for (int e = 0; e < nvalid; ++e) {
-              const uint32_t byte = (qb.nib[e >> 3] >> (8 * ((e >> 1) & 3))) & 0xFFu;
-              const uint32_t nb = (e & 1) ? (byte >> 4) : (byte & 15u);
-              s = fmaf((float)nb - 8.0f, xb[e], s);
-            }
-          }
-          acc[b] = fmaf(qb.d, s, acc[b]);
+      for (int e = t * 4; e < kChunk * kBlock; e += kThreads * 4) {
+        float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (vec && e + 3 < ncol) {
+          q = *reinterpret_cast<const float4 *>(xb + e);
+        } else {
+          if (e < ncol) q.x = xb[e];
+          if (e + 1 < ncol) q.y = xb[e + 1];
+          if (e + 2 < ncol) q.z = xb[e + 2];
+          if (e + 3 < ncol) q.w = xb[e + 3];
         }
+        *reinterpret_cast<float4 *>(&xs[b][e]) = q;
       }
     }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) part[b][t] = acc[b];
     __syncthreads();
-    if (ok && j == 0) {
+    {
+      const int i = 0;
+      uint32_t w0, w1, w2, w3, w4;
+      if (sh[i] == 0) {
+        w0 = v[i].x; w1 = v[i].y; w2 = v[i].z; w3 = v[i].w; w4 = v4[i];
+      } else {
+        w0 = __builtin_amdgcn_alignbyte(v[i].y, v[i].x, 2);
+        w1 = __builtin_amdgcn_alignbyte(v[i].z, v[i].y, 2);
+        w2 = __builtin_amdgcn_alignbyte(v[i].w, v[i].z, 2);
+        w3 = __builtin_amdgcn_alignbyte(v4[i], v[i].w, 2);
+        w4 = v4[i] >> 16;
+      }
+      const float d = half_bits_to_float((uint16_t)(w0 & 0xFFFFu));
+      uint32_t nib[4];                                     // byte k of nib[w]: elements 8w+2k (low), 8w+2k+1 (high)
+      nib[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
+      nib[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
+      nib[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
+      nib[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
+      const int e0 = j * kBlock;                           // column of the block within the chunk
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
-        float s = 0.0f;
-        for (int k = 0; k < P; ++k) s += part[b][rl * P + k];
-        y[(size_t)b * rows + row] = s;
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float4 xa = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w]);
+          const float4 xc = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w + 4]);
+          const uint32_t lo = nib[w] & 0x0F0F0F0Fu;
+          const uint32_t hi = (nib[w] >> 4) & 0x0F0F0F0Fu;
+          s0 = fmaf(ubyte_f<0>(lo) - 8.0f, xa.x, s0);
+          s1 = fmaf(ubyte_f<0>(hi) - 8.0f, xa.y, s1);
+          s0 = fmaf(ubyte_f<1>(lo) - 8.0f, xa.z, s0);
+          s1 = fmaf(ubyte_f<1>(hi) - 8.0f, xa.w, s1);
+          s0 = fmaf(ubyte_f<2>(lo) - 8.0f, xc.x, s0);
+          s1 = fmaf(ubyte_f<2>(hi) - 8.0f, xc.y, s1);
+          s0 = fmaf(ubyte_f<3>(lo) - 8.0f, xc.z, s0);
+          s1 = fmaf(ubyte_f<3>(hi) - 8.0f, xc.w, s1);
+        }
+        acc[b] = fmaf(d, s0 + s1, acc[b]);
       }
     }
-    __syncthreads();
+  }
+  // butterfly over the P lanes of the row (a fixed order: deterministic)
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+    for (int o = P / 2; o >= 1; o >>= 1) acc[b] += __shfl_xor(acc[b], o, P);
+  if (rok && j == 0) {
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) y[(size_t)b * rows + row] = acc[b];
   }
 }
 
@@ -163,28 +177,39 @@ __global__ __launch_bounds__(kThreads) void q4_0_pack_kernel(const float *__rest
   }
 }
 
+template <int BATCH>
+hipError_t launch_batch(const uint8_t *blocks, int rows, int cols, int nblk, uint32_t total,
+                        const float *x, float *y, hipStream_t s) {
+  // lanes per row: the power of two covering the row's blocks (4 .. 64)
+  int P = 4;
+  while (P < 64 && P < nblk) P *= 2;
+  const int grid = (rows + kThreads / P - 1) / (kThreads / P);
+  switch (P) {
+    case 4: q4_0_gemv_kernel<BATCH, 4><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
+    case 8: q4_0_gemv_kernel<BATCH, 8><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
+    case 16: q4_0_gemv_kernel<BATCH, 16><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
+    case 32: q4_0_gemv_kernel<BATCH, 32><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
+    default: q4_0_gemv_kernel<BATCH, 64><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_q4_0_gemv(const uint8_t *blocks, int rows, int cols, const float *x, int batch,
                             float *y, int num_cus, hipStream_t s) {
+  (void)num_cus;
   const int nblk = (cols + kBlock - 1) / kBlock;
-  const int P = nblk < kThreads ? nblk : kThreads;
-  const int R = kThreads / P;
-  const int bpt = (nblk + P - 1) / P;
   const size_t total = (size_t)rows * nblk * kBlockBytes;
-  int grid = (rows + R - 1) / R;
-  if (grid > num_cus * 8) grid = num_cus * 8;
+  if (total >= ((size_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit buffer offsets
   for (int b0 = 0; b0 < batch;) {
     const int nb = batch - b0 >= 4 ? 4 : (batch - b0 >= 2 ? 2 : 1);
     const float *xb = x + (size_t)b0 * cols;
     float *yb = y + (size_t)b0 * rows;
-    if (nb == 4)
-      q4_0_gemv_kernel<4><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, xb, yb, P, R, bpt);
-    else if (nb == 2)
-      q4_0_gemv_kernel<2><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, xb, yb, P, R, bpt);
-    else
-      q4_0_gemv_kernel<1><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, xb, yb, P, R, bpt);
-    const hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (nb == 4) e = launch_batch<4>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
+    else if (nb == 2) e = launch_batch<2>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
+    else e = launch_batch<1>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
     if (e != hipSuccess) return e;
     b0 += nb;
   }
