@@ -430,8 +430,9 @@ hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const Level
   return hipGetLastError();
 }
 
-// Tile shape: the largest of 128x256, 128x128 (m x n) whose tile count still
-// covers the CUs in one round, else 64x128.
+// Tile shape: the largest of 128x256, 128x128, 64x128 (m x n) whose tile count
+// still covers the CUs in one round, else 64x64 (few tokens: the launch is a
+// weight stream and wants every CU on it).
 template <int IB>
 hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                      const int8_t *q, const float *scale, int m, float *y, int num_cus,
@@ -443,7 +444,9 @@ hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTab
     return launch_tiles<IB, 1, 4, 2>(blob, L, T, q, scale, m, y, s);
   if (tiles(128, 128) >= (long)num_cus * 7 / 8)
     return launch_tiles<IB, 2, 2, 2>(blob, L, T, q, scale, m, y, s);
-  return launch_tiles<IB, 2, 1, 2>(blob, L, T, q, scale, m, y, s);
+  if (tiles(64, 128) >= (long)num_cus * 7 / 8)
+    return launch_tiles<IB, 2, 1, 2>(blob, L, T, q, scale, m, y, s);
+  return launch_tiles<IB, 2, 1, 1>(blob, L, T, q, scale, m, y, s);
 }
 
 }  // namespace

@@ -99,7 +99,10 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * (each finite and bfloat16-representable, hence exact in fp16 too;
  * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
- * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128. */
+ * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch > 4 the
+ * product runs on the matrix-core kernel of cq_gemm (one pass over the weights
+ * for all tokens), with its arithmetic: level x norm/4 rounded to fp16 once
+ * per weight, fp32 accumulation. */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
@@ -110,7 +113,11 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * [batch, cols], 16-byte aligned; y [device] fp32 [batch, rows]; q_out
  * [device, may be NULL] int8 [batch, cols] and scale_out [device, may be
  * NULL] fp32 [batch] receive the int8 codes and scales.  Other arguments and
- * limits as cq_gemv, and cols <= 16384. */
+ * limits as cq_gemv, and cols <= 16384.  For batch > 4 the call runs as the
+ * act_fwht_quant_a8 kernel followed by the cq_gemm arithmetic (as cq_gemv does
+ * there); without a 16-byte aligned q_out (or without scale_out) the codes go to
+ * a device buffer the library allocates on first use per device and stream and
+ * keeps, so that first call must not be inside a stream capture. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);
