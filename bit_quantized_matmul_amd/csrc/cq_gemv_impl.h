@@ -260,6 +260,12 @@ __device__ __forceinline__ float quad_xor1(float v) {
 __device__ __forceinline__ float quad_xor2(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
+// Lane i reads lane i^4 of its group of eight: the half-row mirror (i -> 7 - i)
+// followed by the quad reversal (i -> i ^ 3).
+__device__ __forceinline__ float oct_xor4(float v) {
+  const int m = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true);
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+}
 
 // Kernel shape: at most one workgroup per CU (more only for very tall
 // matrices), each finishing a contiguous run of rows.
@@ -284,10 +290,12 @@ __device__ __forceinline__ float quad_xor2(float v) {
 //     fixed order and writes y with coalesced stores.
 //
 // FUSED runs the A8 step on fp32 x with the same fp32 operations as
-// act_fwht_quant_a8: a thread holds one 32-element segment of a group in
-// registers, runs the five in-register butterfly stages, then the two stages
-// across the four lanes of the group with DPP quad permutations; block max,
-// s = max / 127, and the codes go straight from registers to LDS.
+// act_fwht_quant_a8: a thread holds one 16-element segment of a group in
+// registers, runs the four in-register butterfly stages, then the three
+// stages across the eight lanes of the group with DPP permutations (every
+// butterfly is the same a + b, a - b on the same operands, so the values
+// match the other kernel's bit for bit); block max, s = max / 127, and the
+// codes go straight from registers to LDS.
 //
 // Work split: a row slot of P lanes (P = 64, or fewer for short rows) owns a
 // row; its 32-index chunks are dealt out as slot s -> chunk li + P * s.  A
@@ -305,7 +313,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
   constexpr int kWaves = kThreads / kWave;
   constexpr int kCB = 4 * IB;                       // bytes of one chunk
   static_assert(FULL || CPL == 1, "short row slots take one chunk per item");
-  constexpr int SEGS = FUSED ? (BATCH * kMaxFusedCols / kChunk + kThreads - 1) / kThreads : 1;
+  constexpr int kSeg = 16;                          // fused A8: elements a thread holds per segment
+  constexpr int SEGS = FUSED ? (BATCH * kMaxFusedCols / kSeg + kThreads - 1) / kThreads : 1;
   constexpr int QV = FUSED ? 1 : (int)((kMaxActLds / 2 + 16 * kThreads - 1) / (16 * kThreads));
   __shared__ __align__(16) uint8_t tab[TB];
   __shared__ float yblk[kMaxRowsBlk * BATCH];
@@ -381,18 +390,18 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
   // ---- 1. first work item, activations, table, one wait
   issue(ik, ipart, ring[0], nring[0]);
   advance(ik, ipart);
-  float xv[SEGS][FUSED ? 32 : 1];
+  float xv[SEGS][FUSED ? kSeg : 1];
   u32x4 qv[QV];
   uint32_t sclw[BATCH];
-  const int nseg = BATCH * (cols / kChunk);         // 32-element segments (fused)
+  const int nseg = BATCH * (cols / kSeg);           // 16-element segments (fused)
   const int nq = BATCH * cols;                      // int8 codes (unfused)
   if constexpr (FUSED) {
 #pragma unroll
     for (int j = 0; j < SEGS; ++j) {
       if (wave * kWave + j * kThreads >= nseg) continue;   // wave-uniform
-      const uint32_t base = (uint32_t)(t + j * kThreads) * 128u;
+      const uint32_t base = (uint32_t)(t + j * kThreads) * (4u * kSeg);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kSeg / 4; ++e) {
         const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ract, base + 16 * e, 0, 0));
         xv[j][4 * e + 0] = __uint_as_float(w.x);
         xv[j][4 * e + 1] = __uint_as_float(w.y);
@@ -443,20 +452,21 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
 
   // ---- 3. activations -> fp16 pairs in LDS
   if constexpr (FUSED) {
-    const int spr = cols / kChunk;                 // 32-element segments per token
+    const int spr = cols / kSeg;                   // segments per token
     float lmax[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) lmax[b] = 0.0f;
     const float sg1 = (lane & 1) ? -1.0f : 1.0f;
     const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg4 = (lane & 4) ? -1.0f : 1.0f;
 #pragma unroll
     for (int j = 0; j < SEGS; ++j) {
       if (wave * kWave + j * kThreads >= nseg) continue;   // wave-uniform
       float *v = xv[j];
 #pragma unroll
-      for (int h = 1; h < 32; h <<= 1) {
+      for (int h = 1; h < kSeg; h <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < kSeg; ++i) {
           if ((i & h) == 0) {
             const float a = v[i], c = v[i + h];
             v[i] = a + c;
@@ -464,15 +474,17 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
           }
         }
       }
-      // stages 32 and 64: the partner element sits in lane ^ 1 / lane ^ 2; the
-      // lower lane forms a + b, the upper one a - b (its own value is b)
+      // stages 16, 32 and 64: the partner element sits in lane ^ 1, ^ 2, ^ 4;
+      // the lower lane forms a + b, the upper one a - b (its own value is b)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = fmaf(sg1, v[i], quad_xor1(v[i]));
+      for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg1, v[i], quad_xor1(v[i]));
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = fmaf(sg2, v[i], quad_xor2(v[i]));
+      for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg2, v[i], quad_xor2(v[i]));
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg4, v[i], oct_xor4(v[i]));
       float m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+      for (int i = 0; i < kSeg; ++i) m = fmaxf(m, fabsf(v[i]));
       const int bj = (t + j * kThreads) / spr;
 #pragma unroll
       for (int b = 0; b < BATCH; ++b)
@@ -498,15 +510,16 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
     for (int j = 0; j < SEGS; ++j) {
       const int sg = t + j * kThreads;
       if (sg < nseg) {
-        const int b = sg / spr, c = sg - b * spr;
+        const int b = sg / spr, k0 = (sg - b * spr) * kSeg;
+        const int c = k0 >> 5, i0 = (k0 & 31) >> 3;     // chunk, and its first quarter (0 or 2)
         float sc = scs[0], inv = invs[0];
 #pragma unroll
         for (int bb = 1; bb < BATCH; ++bb)
           if (b == bb) { sc = scs[bb]; inv = invs[bb]; }
         // codes in blocks of 8 (bounded register use), packed to fp16 pairs
-        uint32_t pr[16];
+        uint32_t pr[8];
 #pragma unroll
-        for (int k8 = 0; k8 < 4; ++k8) {
+        for (int k8 = 0; k8 < 2; ++k8) {
           float ub[8], cb[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ub[i] = xv[j][8 * k8 + i];
@@ -515,10 +528,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
           for (int p = 0; p < 4; ++p)
             pr[4 * k8 + p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cb[2 * p], cb[2 * p + 1]));
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<uint4 *>(&qs[((b * 4 + i) * C + c) * 4]) =
-              make_uint4(pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]);
+        *reinterpret_cast<uint4 *>(&qs[((b * 4 + i0) * C + c) * 4]) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        *reinterpret_cast<uint4 *>(&qs[((b * 4 + i0 + 1) * C + c) * 4]) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
       }
     }
   } else {
@@ -758,8 +769,9 @@ hipError_t launch_one(const uint8_t *blob, const bqm_cq_layout &L, const LevelTa
 template <int BATCH, int CPL, bool FUSED>
 constexpr int max_pd() {
   constexpr int kThreads = block_threads<CPL>();
-  constexpr int SEGS = FUSED ? (BATCH * kMaxFusedCols / kChunk + kThreads - 1) / kThreads : 1;
-  return (SEGS > 1 ? kRingChunks / 2 : kRingChunks) / CPL;
+  constexpr int kSeg = 16;                          // as in the kernel
+  constexpr int XREGS = FUSED ? (BATCH * kMaxFusedCols / kSeg + kThreads - 1) / kThreads * kSeg : 0;
+  return (XREGS > 32 ? kRingChunks / 2 : kRingChunks) / CPL;
 }
 
 template <int IB, int BATCH, int CPL, bool QREG, bool FUSED>
