@@ -387,9 +387,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
   uint32_t nring[PD][CPL];
   int ik = 0, ipart = 0;
 
-  // ---- 1. first work item, activations, table, one wait
-  issue(ik, ipart, ring[0], nring[0]);
-  advance(ik, ipart);
+  // ---- 1. activations, then the first work item, table, one wait (for the
+  // activations only: the first item's 2 CPL loads may still be in flight)
   float xv[SEGS][FUSED ? kSeg : 1];
   u32x4 qv[QV];
   uint32_t sclw[BATCH];
@@ -422,6 +421,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) sclw[b] = __builtin_amdgcn_raw_buffer_load_b32(rscl, 4 * b, 0, 0);
   }
+  issue(ik, ipart, ring[0], nring[0]);
+  advance(ik, ipart);
   // the replicated level table: a wave instruction writes four rows (16 lanes
   // x 16 bytes each); a lane takes the levels its row needs from lanes 0..15
   // with ds_bpermute
@@ -441,7 +442,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
         *reinterpret_cast<uint4 *>(tab + (4 * u + (lane >> 4)) * 256 + (lane & 15) * 16) = ent[i];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): activations and the first item are in
+  // vmcnt(2 CPL): everything but the first item's loads has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPL));
 
   // ---- 2. the rest of the ring, unconditionally
 #pragma unroll
