@@ -3,11 +3,6 @@
 // compiled in its own cq_gemv_i<IB><f|q>.hip.
 #include "cq_gemv_impl.h"
 
-#include <map>
-#include <mutex>
-#include <utility>
-#include <vector>
-
 namespace bqm {
 
 #define BQM_GEMV_DECL(NAME)                                                                   \
@@ -48,56 +43,16 @@ hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const Lev
   }
 }
 
-namespace {
-
-// Device buffer for the int8 codes and scales of a batched call that has no
-// aligned output of its own, one per (device, stream) so calls on different
-// streams never share it.  It only grows; a replaced buffer is kept (never
-// freed) because a captured graph may still point at it.
-hipError_t a8_workspace(size_t bytes, hipStream_t s, uint8_t **out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
-  static std::vector<void *> retired;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  auto &slot = cache[std::make_pair(dev, s)];
-  if (slot.second < bytes) {
-    void *p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    if (slot.first) retired.push_back(slot.first);
-    slot = std::make_pair(p, bytes);
-  }
-  *out = static_cast<uint8_t *>(slot.first);
-  return hipSuccess;
-}
-
-}  // namespace
-
 hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const float *x, int batch, float *y, int8_t *q_out,
                               float *scale_out, int num_cus, hipStream_t s) {
-  if (batch > 4 && L.idx_bytes < ((int64_t)1 << 30)) {
-    // as launch_cq_gemv: the A8 step, then one matrix-core pass for all tokens
-    const size_t qbytes = (size_t)batch * L.cols;           // a multiple of 128
-    const bool own_q = q_out && ((uintptr_t)q_out & 15u) == 0;
-    const bool own_s = scale_out != nullptr;
-    uint8_t *ws = nullptr;
-    if (!own_q || !own_s) {
-      const hipError_t e = a8_workspace(qbytes + 4 * (size_t)batch, s, &ws);
-      if (e != hipSuccess) return e;
-    }
-    int8_t *q = own_q ? q_out : reinterpret_cast<int8_t *>(ws);
-    float *sc = own_s ? scale_out : reinterpret_cast<float *>(ws + qbytes);
-    hipError_t e = launch_act_fwht_quant_a8(x, batch, L.cols, q, sc, s);
+  if (batch > 4 && L.idx_bytes < ((int64_t)1 << 30) && q_out && scale_out &&
+      ((uintptr_t)q_out & 15u) == 0) {
+    // as launch_cq_gemv: the A8 step into the caller's code and scale buffers,
+    // then one matrix-core pass over the weights for all tokens
+    const hipError_t e = launch_act_fwht_quant_a8(x, batch, L.cols, q_out, scale_out, s);
     if (e != hipSuccess) return e;
-    if (q_out && !own_q) {
-      e = hipMemcpyAsync(q_out, q, qbytes, hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return e;
-    }
-    return launch_cq_gemm(blob, L, T, q, sc, batch, y, num_cus, s);
+    return launch_cq_gemm(blob, L, T, q_out, scale_out, batch, y, num_cus, s);
   }
   switch (L.index_bits) {
     case 1: return gemv_i1f(blob, L, T, nullptr, nullptr, x, q_out, scale_out, batch, y, num_cus, s);

@@ -113,11 +113,10 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * [batch, cols], 16-byte aligned; y [device] fp32 [batch, rows]; q_out
  * [device, may be NULL] int8 [batch, cols] and scale_out [device, may be
  * NULL] fp32 [batch] receive the int8 codes and scales.  Other arguments and
- * limits as cq_gemv, and cols <= 16384.  For batch > 4 the call runs as the
- * act_fwht_quant_a8 kernel followed by the cq_gemm arithmetic (as cq_gemv does
- * there); without a 16-byte aligned q_out (or without scale_out) the codes go to
- * a device buffer the library allocates on first use per device and stream and
- * keeps, so that first call must not be inside a stream capture. */
+ * limits as cq_gemv, and cols <= 16384.  For batch > 4 with both q_out
+ * (16-byte aligned) and scale_out given, the call runs as act_fwht_quant_a8
+ * into them followed by the cq_gemm arithmetic (as cq_gemv does for batch > 4);
+ * otherwise the fused GEMV runs per 4 tokens.  The library allocates nothing. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);
