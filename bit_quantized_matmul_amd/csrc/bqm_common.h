@@ -109,6 +109,10 @@ hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const Lev
 hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const float *x, int batch, float *y, int8_t *q_out,
                               float *scale_out, int num_cus, hipStream_t s);
+bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch);
+hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                              const int8_t *q, const float *scale, int batch, float *y,
+                              int num_cus, hipStream_t s);
 hipError_t launch_cq_gemm(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                           const int8_t *q, const float *scale, int m, float *y, int num_cus,
                           hipStream_t s);

@@ -31,8 +31,11 @@ hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const Lev
                           const int8_t *q, const float *scale, int batch, float *y,
                           int num_cus, hipStream_t s) {
   // Past 4 tokens the dot products, not the weight stream, bound the GEMV (a
-  // launch per 4 tokens re-reads every weight): one pass of the MFMA kernel
-  // over the weights serves all of them.
+  // launch per 4 tokens re-reads every weight): one pass over the weights on
+  // the matrix cores serves all of them (the GEMM kernel where the tokens'
+  // codes do not fit the batched GEMV's LDS).
+  if (batch > 4 && cq_gemv_mma_supported(L, batch))
+    return launch_cq_gemv_mma(blob, L, T, q, scale, batch, y, num_cus, s);
   if (batch > 4 && L.idx_bytes < ((int64_t)1 << 30))
     return launch_cq_gemm(blob, L, T, q, scale, batch, y, num_cus, s);
   switch (L.index_bits) {
@@ -48,11 +51,11 @@ hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const
                               float *scale_out, int num_cus, hipStream_t s) {
   if (batch > 4 && L.idx_bytes < ((int64_t)1 << 30) && q_out && scale_out &&
       ((uintptr_t)q_out & 15u) == 0) {
-    // as launch_cq_gemv: the A8 step into the caller's code and scale buffers,
-    // then one matrix-core pass over the weights for all tokens
+    // the A8 step into the caller's code and scale buffers, then the same
+    // one-pass matrix-core product as launch_cq_gemv
     const hipError_t e = launch_act_fwht_quant_a8(x, batch, L.cols, q_out, scale_out, s);
     if (e != hipSuccess) return e;
-    return launch_cq_gemm(blob, L, T, q_out, scale_out, batch, y, num_cus, s);
+    return launch_cq_gemv(blob, L, T, q_out, scale_out, batch, y, num_cus, s);
   }
   switch (L.index_bits) {
     case 1: return gemv_i1f(blob, L, T, nullptr, nullptr, x, q_out, scale_out, batch, y, num_cus, s);

@@ -100,9 +100,10 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
  * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch > 4 the
- * product runs on the matrix-core kernel of cq_gemm (one pass over the weights
- * for all tokens), with its arithmetic: level x norm/4 rounded to fp16 once
- * per weight, fp32 accumulation. */
+ * product runs on the matrix cores in one pass over the weights for all
+ * tokens: exact fp16 levels x exact fp16 codes, fp32 accumulation per group,
+ * fp32 norm per group (cols <= 4096); for longer rows the cq_gemm kernel and
+ * its arithmetic (level x norm/4 rounded to fp16 once per weight). */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
@@ -115,7 +116,7 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * NULL] fp32 [batch] receive the int8 codes and scales.  Other arguments and
  * limits as cq_gemv, and cols <= 16384.  For batch > 4 with both q_out
  * (16-byte aligned) and scale_out given, the call runs as act_fwht_quant_a8
- * into them followed by the cq_gemm arithmetic (as cq_gemv does for batch > 4);
+ * into them followed by the cq_gemv product for that batch;
  * otherwise the fused GEMV runs per 4 tokens.  The library allocates nothing. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,

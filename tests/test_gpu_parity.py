@@ -132,7 +132,14 @@ def oracle_case(rng, rows, cols, code, batch, codebooks):
 @pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
                                              (300, 512, 3), (70, 4096, 4), (33, 1024, 16),
-                                             (5, 128, 2), (1, 256, 1)])
+                                             (5, 128, 2), (1, 256, 1),
+                                             # 5..16 tokens: one matrix-core pass; K quarters
+                                             # without groups (128, 384), 1..8 row blocks
+                                             # per workgroup with ragged ends, and a K past
+                                             # what its LDS holds (5120: the GEMM route)
+                                             (77, 128, 9), (1000, 384, 5), (300, 4096, 12),
+                                             (5000, 512, 6), (9000, 256, 16), (40000, 128, 7),
+                                             (40, 5120, 8)])
 def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
     rng = np.random.default_rng(400 + code * 7 + rows + batch)
     lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, batch, codebooks)
@@ -146,7 +153,8 @@ def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
 @pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
                                              (1024, 4096, 1), (70, 4096, 4), (33, 1024, 16),
-                                             (5, 128, 2), (1, 256, 1), (200, 4096, 3)])
+                                             (5, 128, 2), (1, 256, 1), (200, 4096, 3),
+                                             (129, 640, 16), (300, 4096, 7)])
 def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
     """One-launch A8 + GEMV: the codes and scales equal the oracle's bit for bit and y
     equals the two-launch path (act_fwht_quant_a8, then cq_gemv) bit for bit."""
