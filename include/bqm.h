@@ -99,25 +99,28 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * (each finite and bfloat16-representable, hence exact in fp16 too;
  * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
- * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch > 4 the
- * product runs on the matrix cores in one pass over the weights for all
- * tokens: exact fp16 levels x exact fp16 codes, fp32 accumulation per group,
- * fp32 norm per group (cols <= 4096); for longer rows the cq_gemm kernel and
- * its arithmetic (level x norm/4 rounded to fp16 once per weight). */
+ * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch >= 2
+ * and cols <= 4096 the product runs on the matrix cores in one pass over the
+ * weights for all tokens: exact fp16 levels x exact fp16 codes, fp32
+ * accumulation per group, fp32 norm per group.  For batch > 4 and longer rows
+ * it runs on the cq_gemm kernel with that kernel's arithmetic (level x norm/4
+ * rounded to fp16 once per weight); otherwise on the VALU GEMV, 4 tokens per
+ * launch. */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
-/* Decode GEMV from fp32 activations: act_fwht_quant_a8 followed by cq_gemv in
- * one launch (same results bit for bit).  Every workgroup quantizes the
- * activations itself while its first weight loads are in flight, so there is
- * no separate activation launch on the decode path.  x [device] fp32
- * [batch, cols], 16-byte aligned; y [device] fp32 [batch, rows]; q_out
- * [device, may be NULL] int8 [batch, cols] and scale_out [device, may be
- * NULL] fp32 [batch] receive the int8 codes and scales.  Other arguments and
- * limits as cq_gemv, and cols <= 16384.  For batch > 4 with both q_out
- * (16-byte aligned) and scale_out given, the call runs as act_fwht_quant_a8
- * into them followed by the cq_gemv product for that batch;
- * otherwise the fused GEMV runs per 4 tokens.  The library allocates nothing. */
+/* Decode GEMV from fp32 activations: act_fwht_quant_a8 then the cq_gemv
+ * product.  x [device] fp32 [batch, cols], 16-byte aligned; y [device] fp32
+ * [batch, rows]; q_out [device, may be NULL] int8 [batch, cols] and scale_out
+ * [device, may be NULL] fp32 [batch] receive the int8 codes and scales.
+ * Other arguments and limits as cq_gemv, and cols <= 16384.  Where cq_gemv
+ * would leave the VALU GEMV (see there) and both q_out (16-byte aligned) and
+ * scale_out are given, the call runs as act_fwht_quant_a8 into them followed
+ * by cq_gemv.  Otherwise one fused launch per 4 tokens: every workgroup
+ * quantizes the activations itself while its first weight loads are in
+ * flight, with the VALU GEMV's arithmetic.  y equals act_fwht_quant_a8 then
+ * cq_gemv bit for bit for batch 1, and whenever q_out and scale_out are
+ * given.  The library allocates nothing. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);

@@ -133,13 +133,14 @@ def oracle_case(rng, rows, cols, code, batch, codebooks):
 @pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
                                              (300, 512, 3), (70, 4096, 4), (33, 1024, 16),
                                              (5, 128, 2), (1, 256, 1),
-                                             # 5..16 tokens: one matrix-core pass; K quarters
+                                             # 2..16 tokens: one matrix-core pass; K eighths
                                              # without groups (128, 384), 1..8 row blocks
-                                             # per workgroup with ragged ends, and a K past
-                                             # what its LDS holds (5120: the GEMM route)
+                                             # per workgroup with ragged ends; past 4096
+                                             # columns the GEMM route (5120 x 8) and the VALU
+                                             # GEMV (5120 x 3)
                                              (77, 128, 9), (1000, 384, 5), (300, 4096, 12),
                                              (5000, 512, 6), (9000, 256, 16), (40000, 128, 7),
-                                             (40, 5120, 8)])
+                                             (40, 5120, 8), (40, 5120, 3)])
 def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
     rng = np.random.default_rng(400 + code * 7 + rows + batch)
     lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, batch, codebooks)
@@ -154,7 +155,7 @@ def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
 @pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
                                              (1024, 4096, 1), (70, 4096, 4), (33, 1024, 16),
                                              (5, 128, 2), (1, 256, 1), (200, 4096, 3),
-                                             (129, 640, 16), (300, 4096, 7)])
+                                             (129, 640, 16), (300, 4096, 7), (50, 5120, 3)])
 def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
     """One-launch A8 + GEMV: the codes and scales equal the oracle's bit for bit and y
     equals the two-launch path (act_fwht_quant_a8, then cq_gemv) bit for bit."""
@@ -180,6 +181,23 @@ def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     ref = omm.cq_reference(idx, n16, 128, code, lv, q_ref, s_ref)
     assert omm.rel_l2(y1, ref) <= TOL
+
+
+@pytest.mark.parametrize("code", [1, 4, 5])
+@pytest.mark.parametrize("rows,cols,batch", [(90, 1024, 3), (33, 4096, 16)])
+def test_cq_gemv_f32_fused_without_code_buffers(code, rows, cols, batch, codebooks):
+    """Several tokens with no q_out / scale_out: the fused launches per 4 tokens."""
+    rng = np.random.default_rng(470 + code + rows + batch)
+    w = weights(rng, rows, cols)
+    x = inputs.activations(rng, batch, cols)
+    lv = levels(code, codebooks)
+    idx, n16 = ocq.encode(w, 128, code, lv)
+    blob = dev(ocq.make_blob(idx, n16, 128, code))
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    y = host(B.cq_gemv_f32(blob, lay, host_codebook(code, codebooks), dev(x)))
+    q_ref, s_ref = oa8.act_quant_a8(x, 128, "fp32")
+    ref = omm.cq_reference(idx, n16, 128, code, lv, q_ref, s_ref)
+    assert omm.rel_l2(y, ref) <= TOL
 
 
 @pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
