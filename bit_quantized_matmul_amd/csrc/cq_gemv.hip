@@ -30,11 +30,11 @@ bool cq_gemv_supported(const bqm_cq_layout &L, bool fused) {
 hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                           const int8_t *q, const float *scale, int batch, float *y,
                           int num_cus, hipStream_t s) {
-  // From 2 tokens on, one pass over the weights on the matrix cores serves
-  // them all (the VALU GEMV re-reads every weight per launch of 4 tokens and
-  // spends its time on the dot products); past 4 tokens, rows longer than the
-  // batched GEMV's register-held codes go to the GEMM kernel.
-  if (batch > 1 && cq_gemv_mma_supported(L, batch))
+  // From 2 tokens on (3 for rows past 4096 columns), one pass over the
+  // weights on the matrix cores serves them all (the VALU GEMV re-reads every
+  // weight per launch of 4 tokens and spends its time on the dot products);
+  // past 4 tokens, rows the batched GEMV does not take go to the GEMM kernel.
+  if (cq_gemv_mma_supported(L, batch))
     return launch_cq_gemv_mma(blob, L, T, q, scale, batch, y, num_cus, s);
   if (batch > 4 && L.idx_bytes < ((int64_t)1 << 30))
     return launch_cq_gemm(blob, L, T, q, scale, batch, y, num_cus, s);
@@ -49,7 +49,7 @@ hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const Lev
 hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const float *x, int batch, float *y, int8_t *q_out,
                               float *scale_out, int num_cus, hipStream_t s) {
-  const bool matrix_cores = (batch > 1 && cq_gemv_mma_supported(L, batch)) ||
+  const bool matrix_cores = cq_gemv_mma_supported(L, batch) ||
                             (batch > 4 && L.idx_bytes < ((int64_t)1 << 30));
   if (matrix_cores && q_out && scale_out && ((uintptr_t)q_out & 15u) == 0) {
     // the A8 step into the caller's code and scale buffers, then the same

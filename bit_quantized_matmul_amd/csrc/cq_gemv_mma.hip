@@ -34,8 +34,8 @@ constexpr int kThreadsV = 512;
 constexpr int kWaves = kThreadsV / 64;  // one per eighth of K
 constexpr int kTok = 16;                // token columns of the MFMA tile
 constexpr int kRBMax = 8;               // row blocks a workgroup finishes
-constexpr int kMaxPD = 4;               // groups of an eighth of K (cols <= 4096)
-constexpr int kMaxCols = kWaves * kMaxPD * kGroup;
+constexpr int kChunkGroups = 32;        // K chunk: the groups whose codes the waves hold at once
+constexpr int kMaxCols = 16384;         // as the fused GEMV's limit
 constexpr int kMaxRings = 2;            // row blocks whose weights are in flight at once
 constexpr int kTabBytes = 65536;        // level table: 256-byte rows
 constexpr int kRedBytes = kWaves * kRBMax * 4 * 64 * 4;   // partial sums [wave][block][r][lane]
@@ -192,88 +192,94 @@ struct MmaArgs {
   uint32_t idx_bytes, norm_bytes;
 };
 
-// PD >= the groups of any eighth of K (ceil(groups / 8)); NRB row blocks of 16
-// rows per workgroup.
-template <int IB, int PD, int NRB>
+// K is taken in chunks of up to kChunkGroups groups (cols <= kChunkGroups *
+// 128 is one chunk).  PD >= the groups of any eighth of a chunk; NRB row
+// blocks of 16 rows per workgroup; CHUNKED: more than one chunk, the tiles
+// (chunk, row block) then run in a loop whose weight loads run two tiles
+// ahead across chunk ends, the next chunk's codes one chunk ahead, and the
+// row blocks' partial sums gather in LDS.
+template <int IB, int PD, int NRB, bool CHUNKED>
 __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, LevelTable T) {
   // one array, the table at its start: table addresses need no base added
   __shared__ __align__(16) uint8_t lds[kTabBytes + kRedBytes];
   uint8_t *const tab = lds;
   float *const red = reinterpret_cast<float *>(lds + kTabBytes);
   const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // the eighth of K
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // the eighth of each chunk
   const int K = A.cols, N = A.rows, ng = K / kGroup;
-  const int g0 = wave * ng / kWaves, ngw = (wave + 1) * ng / kWaves - g0;   // ngw <= PD
+  const int nck = CHUNKED ? (ng + kChunkGroups - 1) / kChunkGroups : 1;
+  const int ntiles = nck * NRB;
   const int row_bytes = K * IB / 8;
   const int h = lane >> 4, l16 = lane & 15;
   const int rb0 = blockIdx.x * NRB;
-  constexpr int R = NRB < kMaxRings ? NRB : kMaxRings;
   const __amdgpu_buffer_rsrc_t ridx = rsrc(A.idx, A.idx_bytes);
   const __amdgpu_buffer_rsrc_t rnrm = rsrc(A.norms, A.norm_bytes);
   const __amdgpu_buffer_rsrc_t rq = rsrc(A.q, (uint32_t)(A.batch * K));
+  // the wave's groups of chunk c: g0 .. g0 + ngw - 1 (ngw <= PD)
+  auto eighth = [&](int c, int &g0, int &ngw) {
+    const int base = c * kChunkGroups;
+    const int ngc = ng - base < kChunkGroups ? ng - base : kChunkGroups;
+    g0 = base + wave * ngc / kWaves;
+    ngw = base + (wave + 1) * ngc / kWaves - g0;
+  };
 
-  // codes: lane (h, l16) takes token l16's codes 32 h .. 32 h + 31 of each
-  // group of the eighth (tokens past the batch read as zeros; slots past the
-  // eighth repeat a group in range, their norm is taken as zero)
-  u32x4v qraw[PD][2];
+  // codes of chunk c: lane (h, l16) takes token l16's codes 32 h .. 32 h + 31
+  // of each group of the eighth (tokens past the batch read as zeros; slots
+  // past the eighth repeat a group in range, their norm is taken as zero)
+  typedef u32x4v Raw[PD][2];
+  auto load_codes = [&](Raw &qraw, int c) {
+    int g0, ngw;
+    eighth(c, g0, ngw);
 #pragma unroll
-  for (int j = 0; j < PD; ++j) {
-    const int g = g0 + j < ng ? g0 + j : ng - 1;
-    const uint32_t off = (uint32_t)(l16 * K + g * kGroup + 32 * h);
-    qraw[j][0] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    qraw[j][1] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
-  }
+    for (int j = 0; j < PD; ++j) {
+      const int g = g0 + j < ng ? g0 + j : ng - 1;
+      const uint32_t off = (uint32_t)(l16 * K + g * kGroup + 32 * h);
+      qraw[j][0] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      qraw[j][1] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+    }
+  };
+  // as fp16 A fragments: step s takes codes 8 s .. 8 s + 7
+  f16x8v a[PD][4];
+  auto convert = [&](const Raw &qraw) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4v &v = qraw[j][s >> 1];
+        uint32_t o[4];
+        i8x4_f16((s & 1) ? v.z : v.x, o[0], o[1]);
+        i8x4_f16((s & 1) ? v.w : v.y, o[2], o[3]);
+        __builtin_memcpy(&a[j][s], o, 16);
+      }
+  };
 
-  // a ring: the lane's weight words and its row's norms (row l16 of block
-  // rb0 + i) for the groups g0 + j, the norms as the NW aligned words that
-  // hold them.  Past the matrix the loads read zeros; past the eighth's
-  // groups they read whatever lies there and the norm is taken as zero.
+  // a ring: tile tt's weight words of the lane and its row's norms (row l16
+  // of block rb0 + tt % NRB, groups g0 + j of chunk tt / NRB), the norms as
+  // the NW aligned words that hold them.  Past the matrix or the tiles the
+  // loads read zeros; past the eighth's groups they read whatever lies there
+  // and the norm is taken as zero.
   constexpr int NW = (PD + 2) / 2;
   typedef uint32_t Ring[PD][IB];
   typedef uint32_t NRing[NW];
-  auto issue = [&](Ring &w, NRing &n, int i) {
-    const int row = (rb0 + i) * 16 + l16;
-    const bool ok = row < N;
+  auto issue = [&](Ring &w, NRing &n, int tt) {
+    int g0, ngw;
+    eighth(tt / NRB, g0, ngw);
+    const int row = (rb0 + tt % NRB) * 16 + l16;
+    const bool ok = row < N && tt < ntiles;
     const uint32_t wbase = ok ? (uint32_t)(row * row_bytes + g0 * (16 * IB) + h * (4 * IB)) : kOOBv;
     const uint32_t nbase = ok ? (uint32_t)(row * ng + g0) * 2u : kOOBv;
 #pragma unroll
     for (int j = 0; j < PD; ++j) load_words<IB>(ridx, wbase + (uint32_t)(j * 16 * IB), w[j]);
     load_words<NW>(rnrm, nbase & ~3u, n);
   };
-  Ring wr[R];
-  NRing nr[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) issue(wr[r], nr[r], r);
-
-  // level table
-  // lanes 0 .. 15 hold the levels' fp16 bits, gathered from there by the
-  // 3- and 4-bit entries
-  uint32_t lv = 0;
-  if constexpr (IB >= 3) {
-#pragma unroll
-    for (int c = 0; c < (1 << IB); ++c) lv = lane == c ? (uint32_t)T.h16[c] : lv;
-  }
-#pragma unroll
-  for (int o = t * 16; o < tab_rows<IB>() * 256; o += kThreadsV * 16)
-    *reinterpret_cast<uint4 *>(tab + o) = entry16<IB>(o >> 8, T, lv);
-
-  // the codes as fp16 A fragments: step s takes codes 8 s .. 8 s + 7
-  f16x8v a[PD][4];
-#pragma unroll
-  for (int j = 0; j < PD; ++j)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4v &v = qraw[j][s >> 1];
-      uint32_t o[4];
-      i8x4_f16((s & 1) ? v.z : v.x, o[0], o[1]);
-      i8x4_f16((s & 1) ? v.w : v.y, o[2], o[3]);
-      __builtin_memcpy(&a[j][s], o, 16);
-    }
-  __syncthreads();
 
   const uint32_t lo = (uint32_t)(lane * entry_b<IB>()) & 255u;
-  // D[token][row] of one row block: lane (h, l16) holds row l16, tokens 4 h + r
-  auto consume = [&](const Ring &w, const NRing &n, int i) {
+  // D[token][row] of tile tt: lane (h, l16) holds row l16, tokens 4 h + r;
+  // added into the row block's partial sums
+  auto consume = [&](const Ring &w, const NRing &n, int tt) {
+    int g0, ngw;
+    eighth(tt / NRB, g0, ngw);
+    const int i = tt % NRB;
     // the norms' halves from group g0 on: the first sits in the high half
     // of word 0 when the row's norms start 2 bytes into a word
     const uint32_t p = (uint32_t)(((rb0 + i) * 16 + l16) * ng + g0) & 1u;
@@ -292,19 +298,67 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
 #pragma unroll
       for (int r = 0; r < 4; ++r) tot[r] = fmaf(nv, acc[r], tot[r]);
     }
+    float *const slot = red + (wave * NRB + i) * 256 + lane;   // [r][lane]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wave * NRB + i) * 4 + r) * 64 + lane] = tot[r];
+    for (int r = 0; r < 4; ++r) {
+      if (CHUNKED && tt >= NRB) tot[r] += slot[r * 64];
+      slot[r * 64] = tot[r];
+    }
   };
 
-  // row block i in ring i % R; once a ring is used, block i + R's loads go
-  // into it (kept in place against the scheduler, which would sink them)
+  constexpr int R = NRB < kMaxRings && !CHUNKED ? NRB : kMaxRings;
+  Raw qraw;
+  load_codes(qraw, 0);
+  Ring wr[R];
+  NRing nr[R];
 #pragma unroll
-  for (int i = 0; i < NRB; ++i) {
-    consume(wr[i % R], nr[i % R], i);
-    if (i + R < NRB) {
-      __builtin_amdgcn_sched_barrier(0);
-      issue(wr[i % R], nr[i % R], i + R);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < R; ++r) issue(wr[r], nr[r], r);
+
+  // level table: lanes 0 .. 15 hold the levels' fp16 bits, gathered from
+  // there by the 3- and 4-bit entries
+  uint32_t lv = 0;
+  if constexpr (IB >= 3) {
+#pragma unroll
+    for (int c = 0; c < (1 << IB); ++c) lv = lane == c ? (uint32_t)T.h16[c] : lv;
+  }
+#pragma unroll
+  for (int o = t * 16; o < tab_rows<IB>() * 256; o += kThreadsV * 16)
+    *reinterpret_cast<uint4 *>(tab + o) = entry16<IB>(o >> 8, T, lv);
+  convert(qraw);
+  if (CHUNKED) load_codes(qraw, 1);
+  __syncthreads();
+
+  if constexpr (!CHUNKED) {
+    // row block i in ring i % R; once a ring is used, block i + R's loads go
+    // into it (kept in place against the scheduler, which would sink them)
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      consume(wr[i % R], nr[i % R], i);
+      if (i + R < NRB) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(wr[i % R], nr[i % R], i + R);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    // tiles in pairs, tile tt in ring tt % 2; at a chunk's first tile its
+    // codes (loaded a chunk ago) become the A fragments and the next chunk's
+    // codes are requested
+    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int tt = t0 + r;
+        if (tt < ntiles) {
+          if (tt > 0 && tt % NRB == 0) {
+            convert(qraw);
+            load_codes(qraw, tt / NRB + 1 < nck ? tt / NRB + 1 : nck - 1);
+          }
+          consume(wr[r], nr[r], tt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(wr[r], nr[r], tt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -327,7 +381,10 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
 }  // namespace
 
 bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch) {
-  return batch <= kTok && L.cols % kGroup == 0 && L.cols <= kMaxCols &&
+  // 2 tokens only where K is one chunk: with chunks the VALU GEMV, which
+  // holds no codes, is as fast for 2
+  const int min_batch = L.cols <= kChunkGroups * kGroup ? 2 : 3;
+  return batch >= min_batch && batch <= kTok && L.cols % kGroup == 0 && L.cols <= kMaxCols &&
          (uint64_t)L.idx_bytes < (1u << 30) && (uint64_t)L.norms_count * 2 < (1u << 30);
 }
 
@@ -352,20 +409,23 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
   A.idx_bytes = (uint32_t)L.idx_bytes;
   A.norm_bytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);
   const int ng = L.cols / kGroup, pd_need = (ng + kWaves - 1) / kWaves;
-  auto with_nrb = [&](auto ib, auto pd) -> hipError_t {
+  auto with_nrb = [&](auto ib, auto pd, auto chunked) -> hipError_t {
     constexpr int IB = decltype(ib)::value, PD = decltype(pd)::value;
+    constexpr bool CH = decltype(chunked)::value;
     switch (nrb) {
-      case 1: cq_gemv_mma_kernel<IB, PD, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 2: cq_gemv_mma_kernel<IB, PD, 2><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 4: cq_gemv_mma_kernel<IB, PD, 4><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      default: cq_gemv_mma_kernel<IB, PD, kRBMax><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 1: cq_gemv_mma_kernel<IB, PD, 1, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 2: cq_gemv_mma_kernel<IB, PD, 2, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 4: cq_gemv_mma_kernel<IB, PD, 4, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      default: cq_gemv_mma_kernel<IB, PD, kRBMax, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
     }
     return hipGetLastError();
   };
   auto go = [&](auto ib) -> hipError_t {
-    if (pd_need > 2) return with_nrb(ib, std::integral_constant<int, 4>{});
-    if (pd_need > 1) return with_nrb(ib, std::integral_constant<int, 2>{});
-    return with_nrb(ib, std::integral_constant<int, 1>{});
+    if (ng > kChunkGroups)
+      return with_nrb(ib, std::integral_constant<int, 4>{}, std::true_type{});
+    if (pd_need > 2) return with_nrb(ib, std::integral_constant<int, 4>{}, std::false_type{});
+    if (pd_need > 1) return with_nrb(ib, std::integral_constant<int, 2>{}, std::false_type{});
+    return with_nrb(ib, std::integral_constant<int, 1>{}, std::false_type{});
   };
   switch (L.index_bits) {
     case 1: return go(std::integral_constant<int, 1>{});

@@ -100,12 +100,13 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
  * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch >= 2
- * and cols <= 4096 the product runs on the matrix cores in one pass over the
- * weights for all tokens: exact fp16 levels x exact fp16 codes, fp32
- * accumulation per group, fp32 norm per group.  For batch > 4 and longer rows
- * it runs on the cq_gemm kernel with that kernel's arithmetic (level x norm/4
- * rounded to fp16 once per weight); otherwise on the VALU GEMV, 4 tokens per
- * launch. */
+ * (>= 3 when cols > 4096) and cols <= 16384 the product runs on the matrix
+ * cores in one pass over the weights for all tokens: exact fp16 levels x
+ * exact fp16 codes, fp32 accumulation per group, fp32 norm per group, the
+ * groups summed in a fixed order.  Batch 1 and 2 otherwise run on the VALU
+ * GEMV; for cols > 16384 batch > 4 runs on the cq_gemm kernel with that
+ * kernel's arithmetic (level x norm/4 rounded to fp16 once per weight) and
+ * smaller batches on the VALU GEMV, 4 tokens per launch. */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 

@@ -266,6 +266,27 @@ def test_full_size_decode_gemv_sampled(rows, cols, codebooks):
     assert omm.rel_l2(y[:, sel], ref) <= TOL
 
 
+# 2..16 tokens on the matrix-core GEMV at full size: one K chunk with 4 and 8
+# row blocks per workgroup (14336 and 30000 rows), and K in chunks of 4096
+# columns with a partial last chunk and 1, 2 and 4 row blocks per workgroup
+@pytest.mark.parametrize("rows,cols,batch,code", [(14336, 4096, 8, 4), (30000, 4096, 5, 1),
+                                                  (4096, 14336, 16, 4), (4096, 14336, 3, 3),
+                                                  (6000, 4224, 12, 2), (9000, 5120, 16, 4)])
+def test_full_size_batched_decode_sampled(rows, cols, batch, code, codebooks):
+    rng = np.random.default_rng(850 + rows + cols + batch)
+    w = inputs.weight_matrix(rng, rows, cols, outliers=True)
+    x = inputs.activations(rng, batch, cols)
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    cb = host_codebook(code, codebooks)
+    blob = B.cq_pack(dev(w), lay, cb)
+    q, s = B.act_fwht_quant_a8(dev(x))
+    y = host(B.cq_gemv(blob, lay, cb, q, s))
+    sel = np.unique(np.concatenate([sampled_rows(rng, rows, 40), np.arange(rows - 3, rows)]))
+    idx, n16 = ocq.split_blob(host(blob), rows, cols, 128, code)
+    ref = omm.cq_reference(idx[sel], n16[sel], 128, code, levels(code, codebooks), host(q), host(s))
+    assert omm.rel_l2(y[:, sel], ref) <= TOL
+
+
 # the prefill shapes (512 tokens, K = 4096), plus shapes that select each
 # GEMM tile (128x256 for 14336 / 14200 outputs, 128x128 for 7168 and for the
 # ragged 300 x 14000, 64x128 for 4096), with ragged tiles in m and n
