@@ -12,11 +12,12 @@ HIP graph and replayed.
 The same line carries: ``roofline`` for the dominant kernel (the fused CQ GEMV
 on the 4096x14336 down-projection shape: mean launch duration over a HIP graph
 of back-to-back HBM-cold launches, timed with HIP events on the launch stream), the prefill GEMM (512 tokens, TFLOP/s), the Minueza-shaped
-Q4_0 decode pass, the bit-width sweep, and ``cpu_baseline``: the CPU oracle
-timed on a bounded sample of the same workload.
+Q4_0 decode pass, the bit-width sweep, the same decode layer shapes at 4 and
+16 tokens per call (``batched_decode_cb4``), and ``cpu_baseline``: the CPU
+oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|sweep|copy   (profiling runs)
+       python bench.py --only dominant|decode|prefill|q4_0|sweep|batched|copy   (profiling runs)
 """
 from __future__ import annotations
 
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "sweep", "copy"])
+    ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "sweep", "batched",
+                                       "copy"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -371,6 +373,37 @@ def bench_sweep(B, torch, dev, cbs, steps):
     return out
 
 
+def bench_batched(B, torch, dev, cbs, steps, batches=(4, 16)):
+    """Several decode tokens at once on the 8B layer shapes (cb4): one cq_gemv per
+    matrix, whose one pass over the weights on the matrix cores serves every token."""
+    from bit_quantized_matmul_amd import inputs
+    rng = inputs.rng_for(11)
+    out = {}
+    for (rows, cols) in inputs.DECODE_8B_SHAPES:
+        w = torch.from_numpy(inputs.weight_matrix(rng, rows, cols, outliers=True)).to(dev)
+        lay = B.cq_pack_info(rows, cols, 128, 4)
+        blob = B.cq_pack(w, lay, cbs[4])
+        del w
+        nb = payload_bytes(lay)
+        n = pool_copies(nb)
+        pool = [blob] + [blob.clone() for _ in range(n - 1)]
+        for batch in batches:
+            x = torch.from_numpy(inputs.activations(rng, batch, cols)).to(dev)
+            q, s = B.act_fwht_quant_a8(x)
+            y = torch.empty((batch, rows), dtype=torch.float32, device=dev)
+            d = graph_mean_ms(torch, [
+                (lambda k=k: B.cq_gemv(pool[k], lay, cbs[4], q, s, y=y))
+                for k in range(n)])
+            out[f"{rows}x{cols}_b{batch}"] = dict(us=d * 1e3, gbps=nb / d / 1e6,
+                                                  frac=nb / d / 1e6 / HBM_PEAK_GBPS)
+        del pool, blob
+        torch.cuda.synchronize()
+    for batch in batches:
+        us = sum(v["us"] for k, v in out.items() if k.endswith(f"_b{batch}"))
+        out[f"step_b{batch}"] = dict(us=us, tokens_per_s=batch / us * 1e6)
+    return out
+
+
 def bench_copy(torch, dev, steps):
     """Plain 1 GiB device copy: the calibration kernel for FETCH_SIZE / WRITE_SIZE."""
     a = torch.empty(POOL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -471,6 +504,9 @@ def main():
     if args.only == "sweep":
         print(json.dumps(bench_sweep(B, torch, dev, cbs, args.steps)))
         return
+    if args.only == "batched":
+        print(json.dumps(bench_batched(B, torch, dev, cbs, args.steps)))
+        return
 
     dec, mats, pool = bench_decode(B, torch, dev, cbs, args.steps, args.warmup)
     log(f"decode step {dec['ms_per_step'] * 1e3:.1f} us, {dec['gbps']:.0f} GB/s")
@@ -487,6 +523,9 @@ def main():
     log(f"q4_0 pass {q4['us_graph']:.1f} us (graph)")
     sweep = bench_sweep(B, torch, dev, cbs, args.steps)
     log("sweep done")
+    bat = bench_batched(B, torch, dev, cbs, args.steps)
+    log(f"batched decode step: 4 tokens {bat['step_b4']['us']:.1f} us, "
+        f"16 tokens {bat['step_b16']['us']:.1f} us")
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     if cpu:
         log(f"cpu baseline {cpu['value']:.4f} GB/s in {cpu['seconds']:.1f} s")
@@ -533,6 +572,7 @@ def main():
         "prefill_gemm": pre,
         "q4_0_minueza_pass": q4,
         "bit_sweep_14336x4096": sweep,
+        "batched_decode_cb4": bat,
     }
     print(json.dumps(line))
 
