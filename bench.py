@@ -6,8 +6,9 @@ layer shapes (CQ W4A8, group 128, batch 1): for each of the four matrices
 quantizes the fp32 activations (A8) inside the GEMV launch.  ``value`` =
 packed weight bytes (indices + fp16 norms) of the step / step time, in GB/s.  Weights are resident in HBM: the step cycles over
 a pool of >= 1 GiB of distinct weight copies, so the 256 MB Infinity Cache
-cannot hold them between uses.  Each pool slot's step is captured once in a
-HIP graph and replayed.
+cannot hold them between uses.  After W warm-up steps, the K timed steps run
+consecutively in one HIP graph (as a decode graph holds every layer's
+launches), each on the next weight copy; the step time is their mean.
 
 The same line carries: ``roofline`` for the dominant kernel (the fused CQ GEMV
 on the 4096x14336 down-projection shape: mean launch duration over a HIP graph
@@ -189,43 +190,40 @@ def bench_decode(B, torch, dev, cbs, steps, warmup):
     cb4 = cbs[4]
     run_step(B, mats, pool, 0, cb4)             # caches device properties before capture
     torch.cuda.synchronize()
-    graphs = []
-    for slot in range(ncopies):
+
+    def graph_of(step_fn, slots):
+        """One HIP graph of consecutive steps (as a model's decode graph holds
+        every layer's launches), so a step pays no graph launch of its own."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            run_step(B, mats, pool, slot, cb4)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % ncopies].replay()
-    torch.cuda.synchronize()
-    t = Timer()
-    t.start()
-    for i in range(steps):
-        graphs[(warmup + i) % ncopies].replay()
-    ms = t.stop_ms() / steps
-    torch.cuda.synchronize()
-    # warm (same slot: weights stay in the Infinity Cache)
-    for _ in range(warmup):
-        graphs[0].replay()
-    t.start()
-    for _ in range(steps):
-        graphs[0].replay()
-    ms_warm = t.stop_ms() / steps
+            for slot in slots:
+                step_fn(B, mats, pool, slot, cb4)
+        return g
+
+    def per_step_ms(step_fn, slots_of):
+        """W untimed warm-up steps, then exactly K timed steps, each run as one
+        graph replay; slots_of(i) is step i's weight copy."""
+        if warmup:
+            gw = graph_of(step_fn, [slots_of(i) for i in range(warmup)])
+            gw.replay()
+            torch.cuda.synchronize()
+            del gw
+        g = graph_of(step_fn, [slots_of(warmup + i) for i in range(steps)])
+        torch.cuda.synchronize()
+        t = Timer()
+        t.start()
+        g.replay()
+        ms = t.stop_ms() / steps
+        del g
+        return ms
+
+    # HBM-cold: the weight copies cycled in order, one per step
+    ms = per_step_ms(run_step, lambda i: i % ncopies)
+    # warm: the same copy every step (its weights stay in the Infinity Cache)
+    ms_warm = per_step_ms(run_step, lambda i: 0)
     # the two-launch variant of the step (A8 and GEMV as separate kernels)
-    g2 = []
-    for slot in range(ncopies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run_step_two_launch(B, mats, pool, slot, cb4)
-        g2.append(g)
-    for i in range(warmup):
-        g2[i % ncopies].replay()
-    t.start()
-    for i in range(steps):
-        g2[(warmup + i) % ncopies].replay()
-    ms_two = t.stop_ms() / steps
-    del g2
+    ms_two = per_step_ms(run_step_two_launch, lambda i: i % ncopies)
+    torch.cuda.synchronize()
     res = dict(ms_per_step=ms, step_bytes=step_bytes, pool_copies=ncopies,
                gbps=step_bytes / ms / 1e6, ms_two_launch=ms_two,
                gbps_two_launch=step_bytes / ms_two / 1e6, ms_warm=ms_warm,
@@ -243,7 +241,6 @@ def bench_decode(B, torch, dev, cbs, steps, warmup):
                                launches=len(cp))
         del cp
     res["gemv_per_matrix"] = per
-    del graphs
     return res, mats, pool
 
 
@@ -549,7 +546,9 @@ def main():
                         "[out,in], group 128, cb4, 1% outlier rows x8; per matrix one launch of "
                         "cq_gemv_f32 (A8 fused into the CQ GEMV); "
                         f"weights cycled over {dec['pool_copies']} HBM-resident copies "
-                        f"({dec['pool_copies'] * dec['step_bytes'] / 2**30:.2f} GiB); step in a HIP graph",
+                        f"({dec['pool_copies'] * dec['step_bytes'] / 2**30:.2f} GiB), one per step; "
+                        f"the timed steps are consecutive in one HIP graph, as a decode graph "
+                        f"holds every layer",
             "step_weight_bytes": dec["step_bytes"],
             "batch": 1,
             "parallelism": "single GPU",
