@@ -13,12 +13,13 @@ launches), each on the next weight copy; the step time is their mean.
 The same line carries: ``roofline`` for the dominant kernel (the fused CQ GEMV
 on the 4096x14336 down-projection shape: mean launch duration over a HIP graph
 of back-to-back HBM-cold launches, timed with HIP events on the launch stream), the prefill GEMM (512 tokens, TFLOP/s), the Minueza-shaped
-Q4_0 decode pass, the bit-width sweep, the same decode layer shapes at 4 and
+Q4_0 decode pass and the same pass as a 512-token prefill (q4_0_gemm), the
+bit-width sweep, the same decode layer shapes at 4 and
 16 tokens per call (``batched_decode_cb4``), and ``cpu_baseline``: the CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|sweep|batched|copy   (profiling runs)
+       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|copy   (profiling runs)
 """
 from __future__ import annotations
 
@@ -54,8 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "sweep", "batched",
-                                       "copy"])
+    ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "q4_0_prefill", "sweep",
+                                       "batched", "copy"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -341,6 +342,51 @@ def bench_q4_0(B, torch, dev, steps, warmup):
                 head_gbps=blocks.numel() / ms_head / 1e6, note="weights in Infinity Cache (13 MB pass)")
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
+
+
+def bench_q4_0_prefill(B, torch, dev, steps, warmup, m=512):
+    """The Minueza Q4_0 pass as prefill: m prompt tokens through the same 71
+    matrices, one q4_0_gemm launch each (fp32 activations, fp32 matrix cores)."""
+    from bit_quantized_matmul_amd import inputs
+    wl = inputs.minueza_q4_0_pass()
+    rng = inputs.rng_for(12)
+    items, flops = [], 0
+    for (label, w) in wl.weights:
+        rows, cols = w.shape
+        blocks = B.q4_0_pack(torch.from_numpy(w).to(dev))
+        x = torch.from_numpy(inputs.activations(rng, m, cols)).to(dev)
+        items.append((label, rows, cols, blocks, x,
+                      torch.empty((m, rows), dtype=torch.float32, device=dev)))
+        flops += 2 * m * rows * cols
+
+    def one_pass():
+        for _, rows, cols, blocks, x, y in items:
+            B.q4_0_gemm(blocks, rows, cols, x, y=y)
+
+    one_pass()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_pass()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t = Timer()
+    t.start()
+    for _ in range(steps):
+        g.replay()
+    ms = t.stop_ms() / steps
+    tf = flops / ms / 1e9
+    # the head alone (32002 x 312: the one launch large enough to fill the chip)
+    _, rows, cols, blocks, x, y = items[-1]
+    d = graph_mean_ms(torch, [(lambda: B.q4_0_gemm(blocks, rows, cols, x, y=y))] * 8)
+    head_tf = 2 * m * rows * cols / d / 1e9
+    return dict(tokens=m, launches=len(items), gflop=flops / 1e9, us_graph=ms * 1e3,
+                tflops=tf, frac=tf / FP32_MFMA_PEAK_TFLOPS, head_us=d * 1e3, head_tflops=head_tf,
+                head_frac=head_tf / FP32_MFMA_PEAK_TFLOPS)
+
+
 def bench_sweep(B, torch, dev, cbs, steps):
     from bit_quantized_matmul_amd import inputs
     wl = inputs.cq_bit_sweep()
@@ -498,6 +544,9 @@ def main():
     if args.only == "q4_0":
         print(json.dumps(bench_q4_0(B, torch, dev, args.steps, args.warmup)))
         return
+    if args.only == "q4_0_prefill":
+        print(json.dumps(bench_q4_0_prefill(B, torch, dev, args.steps, args.warmup)))
+        return
     if args.only == "sweep":
         print(json.dumps(bench_sweep(B, torch, dev, cbs, args.steps)))
         return
@@ -518,6 +567,8 @@ def main():
     log(f"prefill {json.dumps({k: round(v.get('tflops', 0), 1) for k, v in pre.items()})}")
     q4 = bench_q4_0(B, torch, dev, args.steps, args.warmup)
     log(f"q4_0 pass {q4['us_graph']:.1f} us (graph)")
+    q4p = bench_q4_0_prefill(B, torch, dev, args.steps, args.warmup)
+    log(f"q4_0 prefill pass, {q4p['tokens']} tokens: {q4p['us_graph']:.1f} us, {q4p['tflops']:.1f} TFLOP/s")
     sweep = bench_sweep(B, torch, dev, cbs, args.steps)
     log("sweep done")
     bat = bench_batched(B, torch, dev, cbs, args.steps)
@@ -570,6 +621,7 @@ def main():
         "gemv_per_matrix": dec["gemv_per_matrix"],
         "prefill_gemm": pre,
         "q4_0_minueza_pass": q4,
+        "q4_0_minueza_prefill_512": q4p,
         "bit_sweep_14336x4096": sweep,
         "batched_decode_cb4": bat,
     }

@@ -21,7 +21,7 @@ GROUP = 128
 
 EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
-    "cq_gemm", "q4_0_gemv", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
+    "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
 )
 
 
@@ -70,6 +70,7 @@ def load_library() -> ctypes.CDLL:
         "cq_gemv_f32": ([P, LP, F, P, I, P, P, P, P], I),
         "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
         "q4_0_gemv": ([P, I, I, P, I, P, P], I),
+        "q4_0_gemm": ([P, I, I, P, I, P, P], I),
         "cq_pack": ([P, LP, F, P, P, P], I),
         "q4_0_pack": ([P, I, I, P, P], I),
         "cq_codebook_fit": ([P, I64, I, I, P, P, P], I),
@@ -203,6 +204,18 @@ def q4_0_gemv(blocks, rows: int, cols: int, x, y=None):
         y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
     _check("q4_0_gemv", load_library().q4_0_gemv(
         _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), batch,
+        _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def q4_0_gemm(blocks, rows: int, cols: int, x, y=None):
+    """Q4_0 blocks [rows, ceil(cols/32), 18] x fp32 x [m, cols] -> fp32 y [m, rows]."""
+    torch = _torch()
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, rows), dtype=torch.float32, device=x.device)
+    _check("q4_0_gemm", load_library().q4_0_gemm(
+        _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), m,
         _dev(y, torch.float32, "y"), _stream()))
     return y
 

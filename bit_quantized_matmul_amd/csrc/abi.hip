@@ -260,6 +260,20 @@ int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch,
       launch_q4_0_gemv((const uint8_t *)blocks, rows, cols, x, batch, y, cus, (hipStream_t)stream));
 }
 
+int q4_0_gemm(const void *blocks, int rows, int cols, const float *x, int m, float *y,
+              bqm_stream_t stream) {
+  if (!blocks || !x || !y || rows < 1 || cols < 1 || m < 1) return BQM_EINVAL;
+  if (!aligned16(blocks) || !aligned16(x) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
+  const int64_t nblk = ((int64_t)cols + 31) / 32;
+  if ((int64_t)rows * nblk * 18 >= ((int64_t)1 << 31) || (int64_t)m * cols * 4 >= ((int64_t)1 << 31) ||
+      ((int64_t)m + 63) / 64 > 65535)
+    return BQM_ENOTSUP;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_q4_0_gemm((const uint8_t *)blocks, rows, cols, x, m, y, cus, (hipStream_t)stream));
+}
+
 int cq_pack(const float *w, const bqm_cq_layout *layout, const float *codebook, void *blob,
             int32_t *status, bqm_stream_t stream) {
   if (!w || !blob) return BQM_EINVAL;

@@ -118,6 +118,8 @@ hipError_t launch_cq_gemm(const uint8_t *blob, const bqm_cq_layout &L, const Lev
                           hipStream_t s);
 hipError_t launch_q4_0_gemv(const uint8_t *blocks, int rows, int cols, const float *x, int batch,
                             float *y, int num_cus, hipStream_t s);
+hipError_t launch_q4_0_gemm(const uint8_t *blocks, int rows, int cols, const float *x, int m,
+                            float *y, int num_cus, hipStream_t s);
 hipError_t launch_cq_pack(const float *w, const bqm_cq_layout &L, const LevelTable &T,
                           uint8_t *blob, int32_t *status, hipStream_t s);
 hipError_t launch_q4_0_pack(const float *w, int rows, int cols, uint8_t *blocks, hipStream_t s);

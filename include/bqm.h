@@ -148,6 +148,18 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
 int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
               bqm_stream_t stream);
 
+/* Q4_0 prefill GEMM: the q4_0_gemv sum for m tokens (Minueza-32M -> KMCU v1
+ * page, sections 2 and 3, for the blocks; Needle article, section 3: prefill
+ * is a GEMM over the same [out, in] layout).
+ *   y[t, r] = sum_blk sum_{j<32} ((nibble - 8) * d) * x[t, 32 blk + j]
+ * blocks [device] as for q4_0_gemv (16-byte aligned); x [device] fp32
+ * [m, cols], 16-byte aligned (columns >= cols are never read); y [device] fp32
+ * [m, rows].  m >= 1.  Each weight (nibble - 8) * d is formed exactly in fp32
+ * and the matrix cores multiply and accumulate in fp32.  Returns BQM_ENOTSUP
+ * when the blocks or m * cols * 4 bytes reach 2^31 (32-bit offsets). */
+int q4_0_gemm(const void *blocks, int rows, int cols, const float *x, int m, float *y,
+              bqm_stream_t stream);
+
 /* Encode fp32 weights into a CQ blob on the device (Needle article,
  * section 1: group FWHT with the normalized Walsh-Hadamard matrix, nearest
  * Lloyd-Max level per coordinate, fp16 group L2 norm, LSB-first packing).

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_abi():
     names = declared_functions()
     for required in ("cq_pack_info", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32", "cq_gemm", "q4_0_gemv",
-                     "cq_pack", "q4_0_pack", "cq_codebook_fit", "cq_analytic_levels", "bqm_strerror"):
+                     "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "cq_analytic_levels",
+                     "bqm_strerror"):
         assert required in names
 
 
@@ -96,6 +97,10 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
     assert lib.q4_0_gemv(None, 4, 312, p, 1, p, None) == E.BQM_EINVAL
     assert lib.q4_0_gemv(p, 4, 312, p, 17, p, None) == E.BQM_ENOTSUP
+    assert lib.q4_0_gemm(p, 4, 312, p, 0, p, None) == E.BQM_EINVAL
+    assert lib.q4_0_gemm(p, 4, 312, None, 8, p, None) == E.BQM_EINVAL
+    assert lib.q4_0_gemm(p, 4, 312, ctypes.c_void_p(4100), 8, p, None) == E.BQM_EALIGN
+    assert lib.q4_0_gemm(p, 4, 1 << 20, p, 1024, p, None) == E.BQM_ENOTSUP     # m * cols * 4 >= 2^31
     assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL
     assert lib.q4_0_pack(p, 0, 312, p, None) == E.BQM_EINVAL
     assert lib.cq_codebook_fit(p, 1 << 20, 16, 200, None, p, None) == E.BQM_ENOTSUP

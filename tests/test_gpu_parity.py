@@ -227,6 +227,26 @@ def test_q4_0_gemv_parity(rows, cols, batch):
     assert err <= TOL, f"rel L2 {err:.3e}"
 
 
+# the Minueza layer and head shapes at a prompt's worth of tokens, a ragged
+# token count, cols past a whole block (1092) and not a multiple of 4 (33, 101:
+# the 4-byte activation loads), single rows, tokens and columns
+@pytest.mark.parametrize("rows,cols,m", [(312, 312, 37), (104, 312, 512), (1092, 312, 64),
+                                         (312, 1092, 100), (32002, 312, 130), (70, 33, 65),
+                                         (129, 101, 3), (1, 1, 1), (5, 64, 1)])
+def test_q4_0_gemm_parity(rows, cols, m):
+    rng = np.random.default_rng(650 + rows + cols + m)
+    w = inputs.weight_matrix(rng, rows, cols)
+    x = inputs.activations(rng, m, cols)
+    blk = oq4.encode(w)
+    ref = omm.q4_0_reference(blk, cols, x)
+    y = host(B.q4_0_gemm(dev(blk.ravel()), rows, cols, dev(x)))
+    err = omm.rel_l2(y, ref)
+    assert err <= TOL, f"rel L2 {err:.3e}"
+    # every token's row equals the GEMV's sum to fp32 rounding
+    g = host(B.q4_0_gemv(dev(blk.ravel()), rows, cols, dev(x[:1])))
+    assert omm.rel_l2(y[:1], g) <= 1e-5
+
+
 def test_results_are_deterministic(codebooks):
     rng = np.random.default_rng(700)
     lv, idx, n16, blob, q, s = oracle_case(rng, 300, 1024, 4, 40, codebooks)
