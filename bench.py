@@ -19,7 +19,7 @@ bit-width sweep, the same decode layer shapes at 4 and
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|copy   (profiling runs)
+       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|copy   (profiling runs)
 """
 from __future__ import annotations
 
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "q4_0_prefill", "sweep",
-                                       "batched", "copy"])
+                                       "batched", "kmcu", "copy"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -387,6 +387,63 @@ def bench_q4_0_prefill(B, torch, dev, steps, warmup, m=512):
                 head_frac=head_tf / FP32_MFMA_PEAK_TFLOPS)
 
 
+PCIE_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+
+
+def bench_kmcu_load(B, torch, dev, steps):
+    """The tied Minueza image (92 tensors, 12.58 MiB: the file the KMCU page's
+    section 1 prints) built from synthetic weights packed on the device, then
+    parsed and moved into HBM with kmcu_upload_data.  The copy crosses the
+    host link, so it is rated against PCIe, not HBM."""
+    import time
+    from bit_quantized_matmul_amd import inputs, kmcu
+    wl = inputs.minueza_q4_0_pass(seed=3)
+    packed = {lab: (w.shape, B.q4_0_pack(torch.from_numpy(w).to(dev)).cpu().numpy().tobytes())
+              for lab, w in wl.weights}
+    dim = inputs.MINUEZA_HEAD[2]
+    ones = np.ones(dim, "<f4").tobytes()
+
+    def q4(name, lab):
+        (rows, cols), payload = packed[lab]
+        return (name, kmcu.Q4, rows, cols, payload)
+
+    tensors = [q4("tok_embed", "head")]
+    for i in range(inputs.MINUEZA_LAYERS):
+        tensors.append((f"L{i}.in_ln", kmcu.F32, 1, dim, ones))
+        tensors += [q4(f"L{i}.{n}", f"L{i}.{n}") for n in ("q", "k", "v", "o")]
+        tensors.append((f"L{i}.post_ln", kmcu.F32, 1, dim, ones))
+        tensors += [q4(f"L{i}.{n}", f"L{i}.{n}") for n in ("gate", "up", "down")]
+    tensors.append(("final_norm", kmcu.F32, 1, dim, ones))
+    model = dict(n_layers=inputs.MINUEZA_LAYERS, dim=dim, n_heads=12, n_kv_heads=4, head_dim=26,
+                 ffn_dim=1092, vocab_size=32002, max_seq=2048, bos_id=1, eos_id=32000, tied_embed=1,
+                 rope_theta=10000.0, norm_eps=1e-6)
+    file = bytes(kmcu.write(model, tensors))
+    pinned = torch.empty((len(file),), dtype=torch.uint8, pin_memory=True)
+    pinned.numpy()[:] = np.frombuffer(file, np.uint8)
+    h = B.kmcu_header(file)
+    data_bytes = len(file) - h.data_offset
+    dst = torch.empty((data_bytes,), dtype=torch.uint8, device=dev)
+
+    def rate(src):
+        B.kmcu_upload_data(src, dst)                   # warm: page-in, staging buffers
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            B.kmcu_upload_data(src, dst)               # waits for its copy
+        sec = (time.perf_counter() - t0) / steps
+        return sec * 1e6, data_bytes / sec / 1e9
+
+    pageable_us, pageable_gbps = rate(file)
+    pinned_us, pinned_gbps = rate(pinned)
+    t0 = time.perf_counter()
+    _, loaded = B.kmcu_load(pinned)                    # parse + allocate + one copy
+    load_us = (time.perf_counter() - t0) * 1e6
+    ok = all(torch.equal(view.cpu(), pinned[t.offset:t.offset + t.nbytes]) for t, view in loaded.values())
+    return dict(file_mib=len(file) / 2 ** 20, tensors=h.n_tensors, total_params=h.total_params,
+                data_bytes=data_bytes, pageable_us=pageable_us, pageable_gbps=pageable_gbps,
+                pinned_us=pinned_us, pinned_gbps=pinned_gbps, pinned_frac=pinned_gbps / PCIE_PEAK_GBPS,
+                pcie_peak_gbps=PCIE_PEAK_GBPS, kmcu_load_us=load_us, bytes_match=bool(ok))
+
+
 def bench_sweep(B, torch, dev, cbs, steps):
     from bit_quantized_matmul_amd import inputs
     wl = inputs.cq_bit_sweep()
@@ -533,6 +590,9 @@ def main():
     if args.only == "copy":
         print(json.dumps(bench_copy(torch, dev, args.steps)))
         return
+    if args.only == "kmcu":
+        print(json.dumps(bench_kmcu_load(B, torch, dev, args.steps)))
+        return
     cbs = fit_codebooks(B, torch, dev)
     log("codebooks fitted on device")
     if args.only == "dominant":
@@ -574,6 +634,9 @@ def main():
     bat = bench_batched(B, torch, dev, cbs, args.steps)
     log(f"batched decode step: 4 tokens {bat['step_b4']['us']:.1f} us, "
         f"16 tokens {bat['step_b16']['us']:.1f} us")
+    km = bench_kmcu_load(B, torch, dev, args.steps)
+    log(f"kmcu load: {km['file_mib']:.2f} MiB image, pinned {km['pinned_gbps']:.1f} GB/s, "
+        f"pageable {km['pageable_gbps']:.1f} GB/s")
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     if cpu:
         log(f"cpu baseline {cpu['value']:.4f} GB/s in {cpu['seconds']:.1f} s")
@@ -624,6 +687,7 @@ def main():
         "q4_0_minueza_prefill_512": q4p,
         "bit_sweep_14336x4096": sweep,
         "batched_decode_cb4": bat,
+        "kmcu_load_minueza_tied": km,
     }
     print(json.dumps(line))
 

@@ -22,7 +22,9 @@ GROUP = 128
 EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
     "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
+    "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data",
 )
+KMCU_F32, KMCU_Q4 = 1, 2
 
 
 class BqmError(RuntimeError):
@@ -42,6 +44,26 @@ class CqLayout(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+class KmcuHeader(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "version", "n_layers", "dim", "n_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab_size",
+        "max_seq", "bos_id", "eos_id", "tied_embed", "n_tensors", "dir_offset", "data_offset")] + [
+        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("total_params", ctypes.c_uint32)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class KmcuTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 25), ("dtype", ctypes.c_uint32), ("n_rows", ctypes.c_uint32),
+                ("n_cols", ctypes.c_uint32), ("offset", ctypes.c_uint32), ("nbytes", ctypes.c_uint32)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
 
 
 _lib = None
@@ -75,6 +97,11 @@ def load_library() -> ctypes.CDLL:
         "q4_0_pack": ([P, I, I, P, P], I),
         "cq_codebook_fit": ([P, I64, I, I, P, P, P], I),
         "bqm_strerror": ([I], ctypes.c_char_p),
+        "kmcu_header": ([P, ctypes.c_uint64, ctypes.POINTER(KmcuHeader)], I),
+        "kmcu_tensor": ([P, ctypes.c_uint64, I, ctypes.POINTER(KmcuTensor)], I),
+        "kmcu_find": ([P, ctypes.c_uint64, ctypes.c_char_p, ctypes.POINTER(KmcuTensor)], I),
+        "kmcu_upload": ([P, ctypes.c_uint64, ctypes.POINTER(KmcuTensor), P, P], I),
+        "kmcu_upload_data": ([P, ctypes.c_uint64, P, ctypes.c_uint64, P], I),
     }
     for name, (args, ret) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +245,87 @@ def q4_0_gemm(blocks, rows: int, cols: int, x, y=None):
         _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), m,
         _dev(y, torch.float32, "y"), _stream()))
     return y
+
+
+# ---------------------------------------------------------------- KMCU container
+
+def _host_bytes(buf):
+    """A host byte buffer (bytes, bytearray, numpy uint8, CPU torch uint8
+    tensor, pinned or not) -> (pointer, size, keep-alive)."""
+    if isinstance(buf, (bytes, bytearray, memoryview)):
+        arr = np.frombuffer(buf, dtype=np.uint8)
+        return ctypes.c_void_p(arr.ctypes.data), arr.nbytes, arr
+    if not isinstance(buf, np.ndarray):
+        torch = _torch()
+        if isinstance(buf, torch.Tensor):
+            if buf.is_cuda or buf.dtype != torch.uint8 or not buf.is_contiguous():
+                raise ValueError("file must be a contiguous host uint8 tensor")
+            return ctypes.c_void_p(buf.data_ptr()), buf.numel(), buf
+    if buf.dtype != np.uint8 or not buf.flags.c_contiguous:
+        raise ValueError("file must be a contiguous uint8 array")
+    return ctypes.c_void_p(buf.ctypes.data), buf.nbytes, buf
+
+
+def kmcu_header(file) -> KmcuHeader:
+    p, n, _keep = _host_bytes(file)
+    h = KmcuHeader()
+    _check("kmcu_header", load_library().kmcu_header(p, n, ctypes.byref(h)))
+    return h
+
+
+def kmcu_tensor(file, index: int) -> KmcuTensor:
+    p, n, _keep = _host_bytes(file)
+    t = KmcuTensor()
+    _check("kmcu_tensor", load_library().kmcu_tensor(p, n, index, ctypes.byref(t)))
+    return t
+
+
+def kmcu_find(file, name: str) -> KmcuTensor:
+    p, n, _keep = _host_bytes(file)
+    t = KmcuTensor()
+    _check("kmcu_find", load_library().kmcu_find(p, n, name.encode(), ctypes.byref(t)))
+    return t
+
+
+def kmcu_upload(file, tensor: KmcuTensor, dst=None):
+    """Copy one tensor of the file into a device buffer (uint8 [nbytes]); the
+    call waits for the copy, so the file buffer may be released afterwards."""
+    torch = _torch()
+    if dst is None:
+        dst = torch.empty((tensor.nbytes,), dtype=torch.uint8, device="cuda")
+    p, n, _keep = _host_bytes(file)
+    _check("kmcu_upload", load_library().kmcu_upload(p, n, ctypes.byref(tensor),
+                                                     _dev(dst, torch.uint8, "dst"), _stream()))
+    torch.cuda.current_stream().synchronize()
+    return dst
+
+
+def kmcu_upload_data(file, dst=None):
+    """The file's whole data region into one device buffer (uint8), one copy;
+    returns it.  The call waits for the copy."""
+    torch = _torch()
+    p, n, _keep = _host_bytes(file)
+    if dst is None:
+        h = kmcu_header(file)
+        dst = torch.empty((n - h.data_offset,), dtype=torch.uint8, device="cuda")
+    _check("kmcu_upload_data", load_library().kmcu_upload_data(p, n, _dev(dst, torch.uint8, "dst"),
+                                                               dst.numel(), _stream()))
+    torch.cuda.current_stream().synchronize()
+    return dst
+
+
+def kmcu_load(file):
+    """Parse a KMCU v1 file and move its tensors to the device in one copy.
+    Returns (header, {name: (record, uint8 device view of its bytes)}); the
+    views share one allocation, each at its file offset minus data_offset."""
+    h = kmcu_header(file)
+    data = kmcu_upload_data(file)
+    out = {}
+    for i in range(h.n_tensors):
+        t = kmcu_tensor(file, i)
+        start = t.offset - h.data_offset
+        out[t.name.decode()] = (t, data[start:start + t.nbytes])
+    return h, out
 
 
 def cq_pack(w, layout: CqLayout, codebook, blob=None, status=None):

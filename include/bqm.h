@@ -197,6 +197,61 @@ int q4_0_pack(const float *w, int rows, int cols, void *blocks, bqm_stream_t str
 int cq_codebook_fit(const double *samples, int64_t n, int levels, int iters, double *raw,
                     float *table, bqm_stream_t stream);
 
+/* ---- KMCU v1 container (Minueza-32M -> KMCU v1 page, section 4) ----
+ * A little-endian file: a 128-byte header (magic "KMCU", then the u32 fields
+ * below in order from byte 4, rope_theta and norm_eps as f32 at bytes 64 and
+ * 68, total_params at 72), n_tensors 48-byte directory records at dir_offset
+ * (24-byte zero-padded name; u8 dtype at byte 24; u32 n_rows, n_cols,
+ * offset, nbytes at bytes 28, 32, 36, 40), tensor data 64-byte aligned.
+ * n_cols is the count before the Q4_0 rows are padded to 32.  The functions
+ * read the file's bytes where the caller holds them (host memory, read or
+ * mapped) and copy nothing except in kmcu_upload.  Every value handed out is
+ * checked against the file first: a record's dtype is f32 or Q4_0, its nbytes
+ * match its shape (f32: 4 rows cols; Q4_0: 18 rows ceil(cols/32)), its data
+ * is 64-byte aligned, at or after data_offset and inside the file, and
+ * data_offset itself is 64-byte aligned; BQM_EINVAL otherwise, BQM_ENOTSUP
+ * for a version other than 1. */
+enum { BQM_KMCU_F32 = 1, BQM_KMCU_Q4 = 2 };
+
+typedef struct {
+  uint32_t version, n_layers, dim, n_heads, n_kv_heads, head_dim, ffn_dim, vocab_size, max_seq,
+      bos_id, eos_id, tied_embed, n_tensors, dir_offset, data_offset;
+  float rope_theta, norm_eps;
+  uint32_t total_params;
+} bqm_kmcu_header;
+
+typedef struct {
+  char name[25];                  /* the record's 24 name bytes, NUL-terminated */
+  uint32_t dtype;                 /* BQM_KMCU_F32 or BQM_KMCU_Q4 */
+  uint32_t n_rows, n_cols, offset, nbytes;
+} bqm_kmcu_tensor;
+
+/* file [host] size bytes -> the header. */
+int kmcu_header(const void *file, uint64_t size, bqm_kmcu_header *header);
+
+/* Record `index` (0 <= index < n_tensors) of the directory. */
+int kmcu_tensor(const void *file, uint64_t size, int index, bqm_kmcu_tensor *tensor);
+
+/* The first record named `name` (BQM_EINVAL when there is none). */
+int kmcu_find(const void *file, uint64_t size, const char *name, bqm_kmcu_tensor *tensor);
+
+/* Copy the tensor's nbytes from the file [host] into dst [device, 16-byte
+ * aligned, caller-owned], asynchronously on `stream` (the file memory must
+ * stay valid until the copy completes).  A Q4_0 tensor lands as q4_0_gemv /
+ * q4_0_gemm blocks, an f32 one as n_rows x n_cols floats. */
+int kmcu_upload(const void *file, uint64_t size, const bqm_kmcu_tensor *tensor, void *dst,
+                bqm_stream_t stream);
+
+/* The whole data region in one copy: bytes [data_offset, size) of the file
+ * [host] to dst [device, 16-byte aligned, dst_bytes >= size - data_offset,
+ * caller-owned], asynchronously on `stream`, after every record has been
+ * checked.  A tensor then starts at dst + (offset - data_offset); with dst
+ * 64-byte aligned its data keeps the file's 64-byte alignment.  The file
+ * memory must stay valid until the copy completes (pinned host memory makes
+ * it a single DMA transfer). */
+int kmcu_upload_data(const void *file, uint64_t size, void *dst, uint64_t dst_bytes,
+                     bqm_stream_t stream);
+
 /* Human-readable name of an error code (static string). */
 const char *bqm_strerror(int code);
 
