@@ -36,6 +36,12 @@
 //    matrices, 128 x 128, or 64 x 128).  Consecutive tiles (the m-tiles of one
 //    n-block, which share weights) are mapped to the same XCD: hardware deals
 //    workgroups round-robin over the 8 XCDs.
+//  * Norms: a wave's norm load touches one cache line per row (32 per
+//    instruction) for 2 bytes each, as costly as an index load.  When the
+//    group count is a multiple of 8 (K a multiple of 1024), a row's norms for
+//    8 consecutive groups are one aligned 16-byte load, made a round of 8
+//    groups ahead into a second register set; otherwise every group loads its
+//    own.
 #include "bqm_common.h"
 
 namespace bqm {
@@ -140,7 +146,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
-constexpr int kDepth = 3;                  // groups of A and B in flight per thread
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -166,14 +171,17 @@ __device__ __forceinline__ void load_b_half(__amdgpu_buffer_rsrc_t r, uint32_t o
 // Loads run kDepth groups ahead in registers through raw buffer loads (rows
 // past M or N read zeros), all issued unconditionally so the compiler waits
 // for exactly one group's loads at a time; groups past K read zeros too, so
-// the loop runs a whole number of kDepth rounds with no branch.
-template <int IB, int WM, int MB, int NB>
+// the loop runs a whole number of rounds with no branch.  N8: the group count
+// is a multiple of 8 and norms come 8 groups to a load.
+template <int IB, int WM, int MB, int NB, bool N8>
 __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     const uint8_t *__restrict__ idx, const uint16_t *__restrict__ norms,
     const int8_t *__restrict__ q, const float *__restrict__ scale, float *__restrict__ y,
     int M, int N, int K, int tiles_m, int tiles_n, uint32_t idx_bytes, uint32_t norm_bytes,
     LevelTable T) {
   constexpr int TB = table_bytes<IB>();
+  constexpr int kDepth = N8 ? 4 : 3;               // groups of A and B in flight per thread
+  constexpr int kRound = N8 ? 8 : kDepth;          // groups per loop round (unrolled)
   constexpr int WN = 4 / WM;
   constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * WN;
   constexpr int kAV = kBM / 64;                    // 16-byte A loads per thread per group
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   const int mt = tile % tiles_m, nt = tile / tiles_m;
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int ng = K / kGroup;
-  const int rounds = (ng + kDepth - 1) / kDepth;
+  const int rounds = (ng + kRound - 1) / kRound;
   const int row_bytes = K * IB / 8;
   const uint32_t laneoff = (uint32_t)(lane * entry_bytes<IB>()) & 255u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)((size_t)M * K));
@@ -235,13 +243,21 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // Each tile walks the groups from its own starting point (wrapping), so the
   // tiles that share A rows or weight rows read different k-slices at any one
   // time instead of all hitting the same memory channels together.
-  const int rot = (nt * 7 + mt * 3) % ng;
-  // Loop steps past the last group (the loop runs whole rounds of kDepth)
+  // (N8: a multiple of 8, so every round's 8 groups share one aligned norm load)
+  const int rot = N8 ? ((nt * 7 + mt * 3) % (ng / 8)) * 8 : (nt * 7 + mt * 3) % ng;
+  // Loop steps past the last group (the loop runs whole rounds)
   // reload group 0 with a zero norm scale, so they add exact zeros and every
   // load stays unconditional (no branch, no early vmcnt drain).
   auto kgroup = [&](int g) { const int x = g + rot; return g >= ng ? 0 : (x < ng ? x : x - ng); };
   u32x4 apre[kDepth][kAV];
-  uint32_t bpre[kDepth][NB][IB], npre[kDepth][NB];
+  uint32_t bpre[kDepth][NB][IB], npre[N8 ? 1 : kDepth][NB];
+  u32x4 ncur[NB], nnext[NB];                       // N8: norms of this round's and the next round's groups
+  auto issue_norms = [&](int g0, u32x4 (&dst)[NB]) {
+    const int gg = kgroup(g0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      dst[nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, nbase[nb] + 2u * gg, 0, 0));
+  };
   auto issue = [&](int g, int slot) {
     const int gg = kgroup(g);
 #pragma unroll
@@ -251,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       load_b_half<IB>(rb, bbase[nb] + (uint32_t)(gg * 16 * IB), bpre[slot][nb]);
-      npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(rn, (nbase[nb] + 2u * gg) & ~3u, 0, 0);
+      if constexpr (!N8)
+        npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(rn, (nbase[nb] + 2u * gg) & ~3u, 0, 0);
     }
   };
   // one 16-byte A load (16 int8) -> 16 fp16 in LDS buffer buf
@@ -274,6 +291,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  if constexpr (N8) issue_norms(0, ncur);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(d, d);
 #pragma unroll
@@ -303,12 +321,20 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     }
     return o;
   };
-  // group g's norm / 4 as an fp16 pair (scaling by 1/4 is exact); its index
-  // words are read in place from prefetch slot d
-  auto take_group = [&](int g, int d) {
+  // group g's norm / 4 as an fp16 pair (scaling by 1/4 is exact): from
+  // prefetch slot d, or (N8) from this round's or the next round's norms,
+  // where group g is halfword g % 8
+  auto take_group = [&](int g, int d, bool next) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
+      uint32_t nw;
+      if constexpr (N8) {
+        const u32x4 v = next ? nnext[nb] : ncur[nb];
+        const int hw = g & 7;
+        nw = v[hw >> 1] >> ((hw & 1) * 16);
+      } else {
+        nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
+      }
       const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)(g < ng ? 0.25f : 0.0f);
       nq[nb] = h2v{h, h};
     }
@@ -318,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   auto read_a = [&](int buf, int c) {
     return *reinterpret_cast<const f16x8 *>(&As[buf][afrag + 32 * (c % MB) * kAStride + 8 * (c / MB)]);
   };
-  take_group(0, 0);
+  take_group(0, 0, false);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[0][nb], 0, tab, laneoff);
   ar[0] = read_a(0, 0);
@@ -328,8 +354,9 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   __builtin_amdgcn_sched_barrier(0);
   for (int r0 = 0; r0 < rounds; ++r0) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int g = r0 * kDepth + d;
+    for (int d8 = 0; d8 < kRound; ++d8) {
+      const int g = r0 * kRound + d8;
+      const int d = d8 % kDepth;
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int s = c / MB, mb = c % MB;
@@ -339,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (mb == 0) {
           const int sl = s == 3 ? (d + 1) % kDepth : d;   // the last step looks up the next group
-          if (s == 3) take_group(g + 1, sl);
+          if (s == 3) take_group(g + 1, sl, d8 == kRound - 1);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[sl][nb], (s + 1) & 3, tab, laneoff);
         }
@@ -351,12 +378,17 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
         }
         if (c == kChunks - 1) {
           issue(g + kDepth, d);                    // refill this slot, kDepth groups ahead
+          if (N8 && d8 == 0) issue_norms(g + kRound, nnext);
           __syncthreads();
           ar[0] = read_a((g + 1) & 1, 0);
           if (kChunks > 1) ar[1] = read_a((g + 1) & 1, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (N8) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ncur[nb] = nnext[nb];
     }
   }
 
@@ -425,8 +457,12 @@ hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const Level
   const uint16_t *norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
   const uint32_t ib = (uint32_t)L.idx_bytes;
   const uint32_t nbytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);   // whole words (blob pads to 64)
-  cq_gemm_kernel<IB, WM, MB, NB><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
-                                                       tiles_m, tiles_n, ib, nbytes, T);
+  if ((L.cols / kGroup) % 8 == 0)
+    cq_gemm_kernel<IB, WM, MB, NB, true><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+                                                                   tiles_m, tiles_n, ib, nbytes, T);
+  else
+    cq_gemm_kernel<IB, WM, MB, NB, false><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+                                                                    tiles_m, tiles_n, ib, nbytes, T);
   return hipGetLastError();
 }
 

@@ -201,8 +201,12 @@ def test_cq_gemv_f32_fused_without_code_buffers(code, rows, cols, batch, codeboo
 
 
 @pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
+# cols 1024 / 2048 / 3072: group counts that are multiples of 8 (norms 8 groups
+# to a load, 1-3 rounds, tiles starting their walk at different rounds);
+# 1152: 9 groups, the per-group norm path past one round
 @pytest.mark.parametrize("m,rows,cols", [(37, 300, 512), (128, 256, 1024), (1, 100, 128),
-                                         (200, 130, 384), (257, 64, 256)])
+                                         (200, 130, 384), (257, 64, 256), (70, 200, 2048),
+                                         (130, 96, 3072), (33, 50, 1152)])
 def test_cq_gemm_parity(code, m, rows, cols, codebooks):
     rng = np.random.default_rng(500 + code * 11 + m + rows)
     lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, m, codebooks)
