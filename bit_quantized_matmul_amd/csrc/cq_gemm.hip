@@ -240,11 +240,13 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     bbase[nb] = ok ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh + 4 * IB * kh) : kOOB;
     nbase[nb] = ok ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
   }
-  // Each tile walks the groups from its own starting point (wrapping), so the
-  // tiles that share A rows or weight rows read different k-slices at any one
-  // time instead of all hitting the same memory channels together.
-  // (N8: a multiple of 8, so every round's 8 groups share one aligned norm load)
-  const int rot = N8 ? ((nt * 7 + mt * 3) % (ng / 8)) * 8 : (nt * 7 + mt * 3) % ng;
+  // Each n-block walks the groups from its own starting point (wrapping), so
+  // the n-blocks that share A rows read different k-slices at any one time
+  // instead of all hitting the same memory channels together.  The m-tiles of
+  // one n-block (on one XCD) walk in step: they read each weight group at
+  // about the same time, and all but the first find it in L2.  (N8: a
+  // multiple of 8, so every round's 8 groups share one aligned norm load.)
+  const int rot = N8 ? ((nt * 7) % (ng / 8)) * 8 : (nt * 7) % ng;
   // Loop steps past the last group (the loop runs whole rounds)
   // reload group 0 with a zero norm scale, so they add exact zeros and every
   // load stays unconditional (no branch, no early vmcnt drain).
