@@ -251,6 +251,55 @@ def test_q4_0_gemm_parity(rows, cols, m):
     assert omm.rel_l2(y[:1], g) <= 1e-5
 
 
+def test_graph_replays_match_eager(codebooks):
+    """Every compute entry point captured in one HIP graph (as the decode and
+    prefill benchmarks run them): each of three replays, with eager work and
+    synchronisations between them, reproduces the eager results bit for bit."""
+    rng = np.random.default_rng(750)
+    cb = codebooks[4]
+    w = torch.from_numpy(weights(rng, 300, 4096)).to(DEV)
+    lay = B.cq_pack_info(300, 4096, 128, 4)
+    blob = B.cq_pack(w, lay, cb)
+    w3 = torch.from_numpy(weights(rng, 200, 1024)).to(DEV)
+    lay3 = B.cq_pack_info(200, 1024, 128, 3)
+    blob3 = B.cq_pack(w3, lay3, codebooks[3])
+    wq = torch.from_numpy(inputs.weight_matrix(rng, 312, 1092)).to(DEV)
+    blk = B.q4_0_pack(wq)
+    x1, x4 = (dev(inputs.activations(rng, b, 4096)) for b in (1, 4))
+    xp = dev(inputs.activations(rng, 70, 1024))
+    xq, xqm = (dev(inputs.activations(rng, b, 1092)) for b in (1, 37))
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=DEV)
+    y1, y4, yp, yq, yqm = f32(1, 300), f32(4, 300), f32(70, 200), f32(1, 312), f32(37, 312)
+    qp = torch.empty((70, 1024), dtype=torch.int8, device=DEV)
+    sp = f32(70)
+    blob_out = torch.empty_like(blob)
+    outs = [y1, y4, qp, sp, yp, yq, yqm, blob_out]
+
+    def step():
+        B.cq_gemv_f32(blob, lay, cb, x1, y=y1)                 # VALU GEMV, A8 fused
+        B.cq_gemv_f32(blob, lay, cb, x4, y=y4)                 # matrix-core GEMV, 4 tokens
+        B.act_fwht_quant_a8(xp, q=qp, scale=sp)
+        B.cq_gemm(blob3, lay3, codebooks[3], qp, sp, y=yp)
+        B.q4_0_gemv(blk, 312, 1092, xq, y=yq)
+        B.q4_0_gemm(blk, 312, 1092, xqm, y=yqm)
+        B.cq_pack(w, lay, cb, blob=blob_out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()                                        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}, output {i}"
+
+
 def test_results_are_deterministic(codebooks):
     rng = np.random.default_rng(700)
     lv, idx, n16, blob, q, s = oracle_case(rng, 300, 1024, 4, 40, codebooks)
