@@ -13,6 +13,9 @@ mmap article's passage on the CQ format):
   the low nibble holding the even column.
 * Bits codes: 2/3/4 use the fitted codebooks cb2/cb3/cb4; 5 is ternary and 1
   binary, both with analytic levels.
+* Ternary weights also come packed as base-3 digits, five per byte (1.6 bits
+  per weight), where 2-bit fields spend 2 bits (the mmap article's Bonsai
+  notes weigh the two against each other for speed and size).
 
 Readings taken (each listed in the design doc):
 
@@ -32,6 +35,11 @@ Readings taken (each listed in the design doc):
   (u/r equals y/||y|| exactly in real arithmetic.)
 * Layout of a packed blob: the index rows back to back, then the fp16 norms
   [rows][cols/G] starting at the next 64-byte boundary, total rounded up to 64.
+* Base-3 ternary (code 6, same levels and encode as code 5): each group is
+  ceil(G/5) bytes (26 for G = 128); byte j holds the group's indices 5j ..
+  5j+4 as sum_i idx[5j+i] * 3**i (the first index least significant, as in
+  the LSB-first packing); positions past the group end hold digit 1, the zero
+  level.  A row is its groups' bytes back to back.
 """
 from __future__ import annotations
 
@@ -41,9 +49,12 @@ from . import codebook as _cb
 from .fp import fp16_rne
 from .hadamard import fwht_u
 
-BINARY, B2, B3, B4, TERNARY = 1, 2, 3, 4, 5
-INDEX_BITS = {BINARY: 1, B2: 2, B3: 3, B4: 4, TERNARY: 2}
-NUM_LEVELS = {BINARY: 2, B2: 4, B3: 8, B4: 16, TERNARY: 3}
+BINARY, B2, B3, B4, TERNARY, TERNARY_B3 = 1, 2, 3, 4, 5, 6
+# 0: not fixed-width fields (base-3 digits, five per byte)
+INDEX_BITS = {BINARY: 1, B2: 2, B3: 3, B4: 4, TERNARY: 2, TERNARY_B3: 0}
+NUM_LEVELS = {BINARY: 2, B2: 4, B3: 8, B4: 16, TERNARY: 3, TERNARY_B3: 3}
+TRITS_PER_BYTE = 5
+TRIT_PAD = 1          # digit of the positions past a group's end: the zero level
 BLOB_ALIGN = 64
 
 
@@ -56,9 +67,12 @@ def pack_info(rows: int, cols: int, group: int, code: int) -> dict:
     if cols % group:
         raise ValueError("cols must be a multiple of group")
     ib = INDEX_BITS[code]
-    if (cols * ib) % 8:
-        raise ValueError("row does not fill whole bytes")
-    idx_row_bytes = cols * ib // 8
+    if code == TERNARY_B3:
+        idx_row_bytes = (cols // group) * trit_bytes(group)
+    else:
+        if (cols * ib) % 8:
+            raise ValueError("row does not fill whole bytes")
+        idx_row_bytes = cols * ib // 8
     idx_bytes = rows * idx_row_bytes
     norms_offset = _round_up(idx_bytes, BLOB_ALIGN)
     norms_count = rows * (cols // group)
@@ -73,10 +87,17 @@ def _round_up(x: int, a: int) -> int:
     return (x + a - 1) // a * a
 
 
+def trit_bytes(group: int) -> int:
+    """Bytes of one base-3 packed group: five digits a byte."""
+    return -(-group // TRITS_PER_BYTE)
+
+
 def levels_for(code: int, codebooks: dict | None = None) -> np.ndarray:
     """fp32 level table for a bits code (ascending)."""
     if code in (BINARY, TERNARY):
         return _cb.analytic_levels(code)
+    if code == TERNARY_B3:                        # the ternary set, packed base-3
+        return _cb.analytic_levels(TERNARY)
     if codebooks is None or code not in codebooks:
         raise ValueError(f"bits code {code} needs its fitted codebook")
     lv = np.asarray(codebooks[code], dtype=np.float32)
@@ -167,12 +188,45 @@ def unpack_indices(packed: np.ndarray, cols: int, index_bits: int) -> np.ndarray
     return idx.reshape(rows, cols)
 
 
+def pack_trits(idx: np.ndarray, group: int) -> np.ndarray:
+    """Base-3 packing per group: byte j = sum_i idx[5j+i] * 3**i over the
+    group's positions 5j .. 5j+4, positions past the group holding TRIT_PAD."""
+    idx = np.asarray(idx, dtype=np.int64)
+    rows, cols = idx.shape
+    if np.any((idx < 0) | (idx > 2)):
+        raise ValueError("base-3 packing holds indices 0, 1, 2 only")
+    ng, nb = cols // group, trit_bytes(group)
+    digits = np.full((rows, ng, nb * TRITS_PER_BYTE), TRIT_PAD, dtype=np.int64)
+    digits[:, :, :group] = idx.reshape(rows, ng, group)
+    digits = digits.reshape(rows, ng, nb, TRITS_PER_BYTE)
+    value = np.zeros((rows, ng, nb), dtype=np.int64)
+    for i in range(TRITS_PER_BYTE):
+        value += digits[..., i] * 3 ** i
+    return value.astype(np.uint8).reshape(rows, ng * nb)
+
+
+def unpack_trits(packed: np.ndarray, cols: int, group: int) -> np.ndarray:
+    """Inverse of ``pack_trits`` (bytes above 242 are not base-3 digits)."""
+    packed = np.asarray(packed, dtype=np.int64)
+    rows = packed.shape[0]
+    if np.any(packed > 3 ** TRITS_PER_BYTE - 1):
+        raise ValueError("byte value above 242")
+    ng, nb = cols // group, trit_bytes(group)
+    v = packed.reshape(rows, ng, nb)
+    digits = np.zeros((rows, ng, nb, TRITS_PER_BYTE), dtype=np.uint8)
+    for i in range(TRITS_PER_BYTE):
+        digits[..., i] = v % 3
+        v = v // 3
+    return digits.reshape(rows, ng, nb * TRITS_PER_BYTE)[:, :, :group].reshape(rows, cols)
+
+
 def make_blob(idx: np.ndarray, norm16: np.ndarray, group: int, code: int) -> np.ndarray:
     """Assemble the packed blob bytes (indices, 64-aligned fp16 norms)."""
     rows, cols = idx.shape
     info = pack_info(rows, cols, group, code)
     blob = np.zeros(info["total_bytes"], dtype=np.uint8)
-    blob[: info["idx_bytes"]] = pack_indices(idx, info["index_bits"]).ravel()
+    packed = pack_trits(idx, group) if code == TERNARY_B3 else pack_indices(idx, info["index_bits"])
+    blob[: info["idx_bytes"]] = packed.ravel()
     nb = np.ascontiguousarray(norm16, dtype=np.float16).view(np.uint8).ravel()
     blob[info["norms_offset"]: info["norms_offset"] + nb.size] = nb
     return blob
@@ -183,7 +237,8 @@ def split_blob(blob: np.ndarray, rows: int, cols: int, group: int, code: int):
     info = pack_info(rows, cols, group, code)
     blob = np.asarray(blob, dtype=np.uint8)
     packed = blob[: info["idx_bytes"]].reshape(rows, info["idx_row_bytes"])
-    idx = unpack_indices(packed, cols, info["index_bits"])
+    idx = (unpack_trits(packed, cols, group) if code == TERNARY_B3
+           else unpack_indices(packed, cols, info["index_bits"]))
     nb = blob[info["norms_offset"]: info["norms_offset"] + 2 * info["norms_count"]]
     return idx, nb.view(np.float16).reshape(rows, cols // group).copy()
 
@@ -191,7 +246,7 @@ def split_blob(blob: np.ndarray, rows: int, cols: int, group: int, code: int):
 def level_values(idx: np.ndarray, code: int, levels: np.ndarray) -> np.ndarray:
     """cb[idx] in fp64; a ternary field value 3 decodes to 0."""
     lv = np.asarray(levels, dtype=np.float32).astype(np.float64)
-    ext = np.concatenate([lv, np.zeros((1 << INDEX_BITS[code]) - len(lv))])
+    ext = np.concatenate([lv, np.zeros(max(1 << INDEX_BITS[code], len(lv)) - len(lv))])
     return ext[np.asarray(idx, dtype=np.int64)]
 
 

@@ -32,6 +32,65 @@ def test_packing_matches_hand_built_bytes():
         assert np.array_equal(cq.unpack_indices(got, ids.shape[1], b), ids)
 
 
+def test_pack_trits_golden():
+    """Base-3 bytes worked by hand from the packing rule (tests/golden/packing_trits.txt)."""
+    patterns = {"mod3": np.arange(128) % 3, "two": np.full(128, 2), "zero": np.zeros(128, int),
+                "one": np.ones(128, int)}
+    for name, j, value in read_golden_rows("packing_trits.txt"):
+        ids = np.tile(patterns[name], 2).reshape(1, 256).astype(np.uint8)   # two groups
+        got = cq.pack_trits(ids, 128)
+        assert got.shape == (1, 52)
+        assert got[0, int(j)] == int(value), (name, j)
+        assert got[0, 26 + int(j)] == int(value), (name, j)       # the second group's byte j
+        assert np.array_equal(cq.unpack_trits(got, 256, 128), ids)
+
+
+def test_pack_trits_digit_positions():
+    """Digit i of byte j is index 5j+i: brute force over every position of a
+    small group (G = 8: two bytes, the second with two padding digits)."""
+    for p in range(8):
+        for v in (0, 2):
+            ids = np.ones((1, 8), dtype=np.uint8)
+            ids[0, p] = v
+            got = cq.pack_trits(ids, 8).astype(int)[0]
+            j, i = divmod(p, 5)
+            want = [121, 121]                       # all digits 1 (padding too)
+            want[j] += (v - 1) * 3 ** i
+            assert list(got) == want, (p, v)
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, 3, size=(5, 384)).astype(np.uint8)
+    packed = cq.pack_trits(ids, 128)
+    assert packed.max() <= 242 and packed.shape == (5, 3 * 26)
+    assert np.array_equal(cq.unpack_trits(packed, 384, 128), ids)
+    with pytest.raises(ValueError):
+        cq.unpack_trits(np.full((1, 26), 243, np.uint8), 128, 128)
+    with pytest.raises(ValueError):
+        cq.pack_trits(np.full((1, 128), 3, np.uint8), 128)
+
+
+def test_ternary_b3_blob_decodes_like_the_2bit_blob():
+    """Codes 5 and 6 share levels and encode; only the packing differs, so the
+    two blobs decode to the same weights and the layouts differ only in size."""
+    rng = np.random.default_rng(66)
+    w = (rng.standard_normal((9, 512)) * 0.02).astype(np.float32)
+    lv = cq.levels_for(cq.TERNARY)
+    assert np.array_equal(cq.levels_for(cq.TERNARY_B3), lv)
+    i5, n5 = cq.encode(w, 128, cq.TERNARY, lv)
+    i6, n6 = cq.encode(w, 128, cq.TERNARY_B3, lv)
+    assert np.array_equal(i5, i6) and np.array_equal(n5, n6)
+    b6 = cq.make_blob(i6, n6, 128, cq.TERNARY_B3)
+    ri, rn = cq.split_blob(b6, 9, 512, 128, cq.TERNARY_B3)
+    assert np.array_equal(ri, i6) and np.array_equal(rn, n6)
+    w5 = cq.decode(i5, n5, 128, cq.TERNARY, lv)
+    w6 = cq.decode(ri, rn, 128, cq.TERNARY_B3, lv)
+    assert np.array_equal(w5, w6)
+    info = cq.pack_info(14336, 4096, 128, cq.TERNARY_B3)
+    assert info["idx_row_bytes"] == 32 * 26 and info["index_bits"] == 0 and info["levels"] == 3
+    # 26 index bytes + a 2-byte norm per 128 weights: 1.75 bits per weight, against 2.125
+    bpw = lambda c: 8 * (cq.pack_info(1, 128, 128, c)["idx_row_bytes"] + 2) / 128
+    assert bpw(cq.TERNARY_B3) == 1.75 and bpw(cq.TERNARY) == 2.125
+
+
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
 def test_pack_roundtrip_and_bit_positions(b):
     rng = np.random.default_rng(b)
@@ -58,7 +117,10 @@ def test_pack_info_sizes():
     with pytest.raises(ValueError):
         cq.pack_info(4, 100, 128, 4)          # cols not a multiple of group
     with pytest.raises(ValueError):
-        cq.pack_info(4, 128, 128, 6)          # unknown bits code
+        cq.pack_info(4, 128, 128, 7)          # unknown bits code
+    # base-3 ternary: 14336 x 32 groups x 26 bytes + norms
+    b3 = cq.pack_info(14336, 4096, 128, 6)
+    assert b3["idx_bytes"] + 2 * b3["norms_count"] == 14336 * 32 * 28 == 12_845_056
 
 
 @pytest.mark.parametrize("code,g", [(cq.BINARY, 8), (cq.TERNARY, 8), (cq.B2, 8), (cq.B3, 4), (cq.B4, 4)])
