@@ -150,7 +150,7 @@ def fit_codebooks(B, torch, dev):
 
 
 def codebook_for(code, cbs):
-    return None if code in (1, 5) else cbs[code]
+    return None if code in (1, 5, 6) else cbs[code]
 
 
 def decode_setup(B, torch, dev, cbs):
@@ -450,9 +450,9 @@ def bench_sweep(B, torch, dev, cbs, steps):
     w = torch.from_numpy(wl.weights[0][1]).to(dev)
     rows, cols = w.shape
     acts = [torch.from_numpy(a).to(dev) for a in wl.acts]
-    names = {1: "binary", 2: "cb2", 3: "cb3", 4: "cb4", 5: "ternary"}
+    names = {1: "binary", 2: "cb2", 3: "cb3", 4: "cb4", 5: "ternary", 6: "ternary_base3"}
     out = {}
-    for code in (1, 2, 3, 4, 5):
+    for code in (1, 2, 3, 4, 5, 6):
         lay = B.cq_pack_info(rows, cols, 128, code)
         cb = codebook_for(code, cbs)
         blob = B.cq_pack(w, lay, cb)
@@ -461,6 +461,8 @@ def bench_sweep(B, torch, dev, cbs, steps):
         pool = [blob] + [blob.clone() for _ in range(n - 1)]
         for a in acts:
             batch = a.shape[0]
+            if code == 6 and batch > 1:                # base-3 ternary: one token only
+                continue
             q, s = B.act_fwht_quant_a8(a)
             y = torch.empty((batch, rows), dtype=torch.float32, device=dev)
             d = graph_mean_ms(torch, [

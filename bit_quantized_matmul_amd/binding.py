@@ -15,7 +15,7 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbqm.so")
 
 BQM_OK, BQM_EINVAL, BQM_EALIGN, BQM_ENOTSUP, BQM_EDEVICE, BQM_ERANGE = 0, -1, -2, -3, -4, -5
-BINARY, B2, B3, B4, TERNARY = 1, 2, 3, 4, 5
+BINARY, B2, B3, B4, TERNARY, TERNARY_B3 = 1, 2, 3, 4, 5, 6
 STATUS_NONFINITE, STATUS_NORM_OVERFLOW = 1, 2
 GROUP = 128
 

@@ -55,7 +55,7 @@ int index_bits_of(int bits) {
     case BQM_CQ_B3: return 3;
     case BQM_CQ_B4: return 4;
     case BQM_CQ_TERNARY: return 2;
-    default: return 0;
+    default: return 0;                           // base-3 ternary too: not fixed-width fields
   }
 }
 
@@ -65,7 +65,8 @@ int levels_of(int bits) {
     case BQM_CQ_B2: return 4;
     case BQM_CQ_B3: return 8;
     case BQM_CQ_B4: return 16;
-    case BQM_CQ_TERNARY: return 3;
+    case BQM_CQ_TERNARY:
+    case BQM_CQ_TERNARY_B3: return 3;
     default: return 0;
   }
 }
@@ -101,7 +102,7 @@ int make_table(int bits, const float *codebook, LevelTable *T) {
   T->bits = bits;
   T->index_bits = index_bits_of(bits);
   T->levels = levels_of(bits);
-  if (bits == BQM_CQ_BINARY || bits == BQM_CQ_TERNARY) {
+  if (bits == BQM_CQ_BINARY || bits == BQM_CQ_TERNARY || bits == BQM_CQ_TERNARY_B3) {
     if (codebook != nullptr) return BQM_EINVAL;
     const double c = bits == BQM_CQ_BINARY ? binary_level() : ternary_level();
     const float cf = (float)c;
@@ -149,10 +150,11 @@ extern "C" {
 int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout) {
   if (!layout) return BQM_EINVAL;
   const int ib = index_bits_of(bits);
-  if (ib == 0) return BQM_EINVAL;
+  const bool base3 = bits == BQM_CQ_TERNARY_B3;
+  if (ib == 0 && !base3) return BQM_EINVAL;
   if (rows < 1 || cols < 1 || group < 2 || (group & (group - 1)) != 0) return BQM_EINVAL;
   if (cols % group != 0) return BQM_EINVAL;
-  if (((int64_t)cols * ib) % 8 != 0) return BQM_EINVAL;
+  if (!base3 && ((int64_t)cols * ib) % 8 != 0) return BQM_EINVAL;
   bqm_cq_layout L;
   memset(&L, 0, sizeof(L));
   L.rows = rows;
@@ -161,7 +163,8 @@ int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout)
   L.bits = bits;
   L.index_bits = ib;
   L.levels = levels_of(bits);
-  L.idx_row_bytes = (int64_t)cols * ib / 8;
+  // base-3: ceil(group / 5) bytes a group
+  L.idx_row_bytes = base3 ? (int64_t)(cols / group) * ((group + 4) / 5) : (int64_t)cols * ib / 8;
   L.idx_bytes = (int64_t)rows * L.idx_row_bytes;
   L.norms_offset = (L.idx_bytes + 63) / 64 * 64;
   L.norms_count = (int64_t)rows * (cols / group);
@@ -171,7 +174,8 @@ int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout)
 }
 
 int cq_analytic_levels(int bits, float *levels) {
-  if (!levels || (bits != BQM_CQ_BINARY && bits != BQM_CQ_TERNARY)) return BQM_EINVAL;
+  if (!levels || (bits != BQM_CQ_BINARY && bits != BQM_CQ_TERNARY && bits != BQM_CQ_TERNARY_B3))
+    return BQM_EINVAL;
   LevelTable T;
   make_table(bits, nullptr, &T);
   for (int l = 0; l < T.levels; ++l) levels[l] = T.f32[l];
@@ -198,12 +202,16 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  if (batch > 16 || !cq_gemv_supported(*layout, false)) return BQM_ENOTSUP;
+  const bool base3 = layout->bits == BQM_CQ_TERNARY_B3;
+  if (base3 ? !cq_gemv_t3_supported(*layout, batch) : (batch > 16 || !cq_gemv_supported(*layout, false)))
+    return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;
   int cus;
   rc = current_device(&cus);
   if (rc) return rc;
+  if (base3)
+    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q, scale, y, cus, (hipStream_t)stream));
   return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
                                   (hipStream_t)stream));
 }
@@ -217,13 +225,24 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  if (batch > 16 || !cq_gemv_supported(*layout, true)) return BQM_ENOTSUP;
+  const bool base3 = layout->bits == BQM_CQ_TERNARY_B3;
+  // base-3: the A8 step goes to the caller's code buffers, then the product
+  if (base3 ? (!cq_gemv_t3_supported(*layout, batch) || !q_out || !scale_out ||
+               layout->cols > 65536)
+            : (batch > 16 || !cq_gemv_supported(*layout, true)))
+    return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(x) || ((uintptr_t)q_out & 3u) || ((uintptr_t)scale_out & 3u) ||
-      ((uintptr_t)y & 3u))
+      ((uintptr_t)y & 3u) || (base3 && !aligned16(q_out)))
     return BQM_EALIGN;
   int cus;
   rc = current_device(&cus);
   if (rc) return rc;
+  if (base3) {
+    const hipError_t e = launch_act_fwht_quant_a8(x, 1, layout->cols, q_out, scale_out, (hipStream_t)stream);
+    if (e != hipSuccess) return BQM_EDEVICE;
+    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q_out, scale_out, y, cus,
+                                       (hipStream_t)stream));
+  }
   return status_of(launch_cq_gemv_f32((const uint8_t *)blob, *layout, T, x, batch, y, q_out,
                                       scale_out, cus, (hipStream_t)stream));
 }
@@ -236,8 +255,10 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
   LevelTable T;
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
-  // the kernel addresses the weights and activations with 32-bit offsets
-  if (layout->idx_bytes >= (int64_t)1 << 30 || (int64_t)m * layout->cols >= (int64_t)1 << 30)
+  // the kernel addresses the weights and activations with 32-bit offsets;
+  // base-3 ternary has a decode product only
+  if (layout->bits == BQM_CQ_TERNARY_B3 || layout->idx_bytes >= (int64_t)1 << 30 ||
+      (int64_t)m * layout->cols >= (int64_t)1 << 30)
     return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;

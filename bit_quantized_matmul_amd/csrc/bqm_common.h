@@ -10,6 +10,8 @@ namespace bqm {
 
 constexpr int kWave = 64;
 constexpr int kGroup = 128;          // CQ quant group (the only one the device path builds)
+constexpr int kTritsPerByte = 5;     // base-3 ternary: five indices a byte
+constexpr int kTritBytes = (kGroup + kTritsPerByte - 1) / kTritsPerByte;   // 26 bytes a group
 constexpr int kChunk = 32;           // indices a lane handles per load in the CQ kernels
 
 // Level table handed to the CQ kernels by value.  For the fitted codebooks
@@ -22,8 +24,8 @@ struct LevelTable {
   uint16_t b16[16];
   float f32[16];    // fp32 levels (cb or c*sign), used by the encoder
   float cscale;
-  int bits;         // bits code 1..5
-  int index_bits;   // 1..4
+  int bits;         // bits code 1..6
+  int index_bits;   // 1..4; 0 for base-3 ternary (five indices a byte)
   int levels;       // 2, 4, 8, 16 or 3
 };
 
@@ -110,6 +112,11 @@ hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const
                               const float *x, int batch, float *y, int8_t *q_out,
                               float *scale_out, int num_cus, hipStream_t s);
 bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch);
+// Base-3 packed ternary (bits code 6): one token, up to 128 groups a row.
+bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch);
+hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                             const int8_t *q, const float *scale, float *y, int num_cus,
+                             hipStream_t s);
 hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const int8_t *q, const float *scale, int batch, float *y,
                               int num_cus, hipStream_t s);

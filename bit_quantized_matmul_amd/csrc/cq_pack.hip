@@ -19,6 +19,10 @@
 // One wave per group: lane l holds u[l] and u[l+64]; stages h = 1..32 swap
 // with lane l^h, stage 64 is inside the lane.  The norm sum runs on lane 0 in
 // index order; lanes 0..15 then each pack one unit of 8 indices.
+//
+// Base-3 ternary (ib == 0, same levels and indices as the 2-bit ternary
+// code): lanes 0..25 each write one byte, sum_i idx[5 lane + i] * 3^i, with
+// digit 1 (the zero level) at the positions past the group's 128.
 #include "bqm_common.h"
 
 namespace bqm {
@@ -36,7 +40,7 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
 
 __global__ __launch_bounds__(kThreads) void cq_pack_kernel(
     const float *__restrict__ w, int rows, int cols, int ib, uint8_t *__restrict__ blob,
-    int64_t norms_offset, int64_t idx_bytes, int64_t total_bytes, LevelTable T,
+    int64_t row_bytes, int64_t norms_offset, int64_t idx_bytes, int64_t total_bytes, LevelTable T,
     int32_t *__restrict__ status) {
   __shared__ double ubuf[kWaves][kGroup];
   __shared__ double ssbuf[kWaves];
@@ -46,7 +50,6 @@ __global__ __launch_bounds__(kThreads) void cq_pack_kernel(
   const int wave = t >> 6;
   const int ng = cols / kGroup;
   const long total = (long)rows * ng;
-  const int64_t row_bytes = (int64_t)cols * ib / 8;
   uint16_t *norms = reinterpret_cast<uint16_t *>(blob + norms_offset);
   const double sqrt_g = __builtin_sqrt(128.0);
 
@@ -112,7 +115,17 @@ __global__ __launch_bounds__(kThreads) void cq_pack_kernel(
     ibuf[wave][lane + 64] = (uint8_t)ibb;
     __syncthreads();
     if (valid) {
-      if (lane < 16) {
+      if (ib == 0) {
+        if (lane < kTritBytes) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int i = kTritsPerByte - 1; i >= 0; --i) {
+            const int p = kTritsPerByte * lane + i;
+            v = 3u * v + (p < kGroup ? (uint32_t)ibuf[wave][p] : 1u);
+          }
+          blob[(int64_t)row * row_bytes + (int64_t)gi * kTritBytes + lane] = (uint8_t)v;
+        }
+      } else if (lane < 16) {
         uint64_t word = 0;
 #pragma unroll
         for (int s = 0; s < 8; ++s) word |= (uint64_t)ibuf[wave][8 * lane + s] << (ib * s);
@@ -143,8 +156,8 @@ hipError_t launch_cq_pack(const float *w, const bqm_cq_layout &L, const LevelTab
   if (grid > 16384) grid = 16384;
   if (grid < 1) grid = 1;
   cq_pack_kernel<<<(int)grid, kThreads, 0, s>>>(w, L.rows, L.cols, L.index_bits, blob,
-                                                 L.norms_offset, L.idx_bytes, L.total_bytes, T,
-                                                 status);
+                                                 L.idx_row_bytes, L.norms_offset, L.idx_bytes,
+                                                 L.total_bytes, T, status);
   return hipGetLastError();
 }
 

@@ -47,8 +47,12 @@ enum {
  * cb2/cb3/cb4 (4, 8, 16 levels); 5 is ternary {-c, 0, +c} and 1 binary
  * {-sqrt(2/pi), +sqrt(2/pi)}, both analytic and built into the library
  * ("Parse-free loading: mmap tensors and Needle's cold start", passage on
- * the CQ format). */
-enum { BQM_CQ_BINARY = 1, BQM_CQ_B2 = 2, BQM_CQ_B3 = 3, BQM_CQ_B4 = 4, BQM_CQ_TERNARY = 5 };
+ * the CQ format).  6 is an addition: the ternary set with its indices packed
+ * as base-3 digits, five to a byte (the llama.cpp TV-box / iPad page weighs
+ * base-3 digits against 2-bit fields for ternary weights in its speed-up
+ * table, section 18). */
+enum { BQM_CQ_BINARY = 1, BQM_CQ_B2 = 2, BQM_CQ_B3 = 3, BQM_CQ_B4 = 4, BQM_CQ_TERNARY = 5,
+       BQM_CQ_TERNARY_B3 = 6 };
 
 /* Status-word bits written by the encoders (OR-ed, never cleared). */
 enum { BQM_STATUS_NONFINITE = 1, BQM_STATUS_NORM_OVERFLOW = 2 };
@@ -63,7 +67,11 @@ enum { BQM_STATUS_NONFINITE = 1, BQM_STATUS_NORM_OVERFLOW = 2 };
  *   [norms_offset, +2*norms_count)  fp16 group L2 norms [rows][cols/group];
  *   total_bytes               rounded up to 64 (the .cact 64-byte blob
  *                             alignment, Needle article, section 2).
- * Ternary uses 2-bit fields holding 0/1/2 (field value 3 decodes to 0). */
+ * Ternary uses 2-bit fields holding 0/1/2 (field value 3 decodes to 0).
+ * Base-3 ternary (bits 6, index_bits 0): each group is ceil(group/5) bytes
+ * (26 for 128), byte j = sum_i idx[5j+i] * 3^i over the group's positions
+ * 5j .. 5j+4 (the first index least significant), positions past the group
+ * holding digit 1 (the zero level); a row is its groups back to back. */
 typedef struct {
   int32_t rows, cols, group, bits, index_bits, levels;
   int64_t idx_row_bytes, idx_bytes, norms_offset, norms_count, total_bytes;
@@ -74,9 +82,9 @@ typedef struct {
  * access.  BQM_EINVAL on a bad shape, group or code. */
 int cq_pack_info(int rows, int cols, int group, int bits, bqm_cq_layout *layout);
 
-/* Built-in levels of the analytic sets: bits 1 -> 2 values, bits 5 -> 3
- * values, ascending fp32, written to `levels` [host].  BQM_EINVAL for other
- * codes.  Host only. */
+/* Built-in levels of the analytic sets: bits 1 -> 2 values, bits 5 and 6 ->
+ * 3 values, ascending fp32, written to `levels` [host].  BQM_EINVAL for
+ * other codes.  Host only. */
 int cq_analytic_levels(int bits, float *levels);
 
 /* Per-token symmetric int8 activations in the rotated domain
@@ -106,7 +114,10 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * groups summed in a fixed order.  Batch 1 and 2 otherwise run on the VALU
  * GEMV; for cols > 16384 batch > 4 runs on the cq_gemm kernel with that
  * kernel's arithmetic (level x norm/4 rounded to fp16 once per weight) and
- * smaller batches on the VALU GEMV, 4 tokens per launch. */
+ * smaller batches on the VALU GEMV, 4 tokens per launch.
+ * Base-3 ternary (bits 6): batch 1 and cols <= 16384 only (BQM_ENOTSUP
+ * otherwise); the group sums of digit x code are exact int32 dot products,
+ * scaled by the fp32 norm and summed in fp32. */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
@@ -121,7 +132,9 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * quantizes the activations itself while its first weight loads are in
  * flight, with the VALU GEMV's arithmetic.  y equals act_fwht_quant_a8 then
  * cq_gemv bit for bit for batch 1, and whenever q_out and scale_out are
- * given.  The library allocates nothing. */
+ * given.  The library allocates nothing.  Base-3 ternary (bits 6): batch 1,
+ * and q_out (16-byte aligned) and scale_out are required (BQM_ENOTSUP
+ * without them): act_fwht_quant_a8 into them, then the cq_gemv product. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);
@@ -134,7 +147,8 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
  * activations enter as exact fp16 integers; the matrix cores accumulate in
  * fp32 and the token scale is applied in fp32.  m >= 1, group must be 128.
  * Returns BQM_ENOTSUP when the packed indices or m * cols exceed 2^30 bytes
- * (the kernel addresses them with 32-bit offsets). */
+ * (the kernel addresses them with 32-bit offsets), and for base-3 ternary
+ * (bits 6), which has a decode product only. */
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int m, float *y, bqm_stream_t stream);
 

@@ -14,8 +14,10 @@ mmap article's passage on the CQ format):
 * Bits codes: 2/3/4 use the fitted codebooks cb2/cb3/cb4; 5 is ternary and 1
   binary, both with analytic levels.
 * Ternary weights also come packed as base-3 digits, five per byte (1.6 bits
-  per weight), where 2-bit fields spend 2 bits (the mmap article's Bonsai
-  notes weigh the two against each other for speed and size).
+  per weight), where 2-bit fields spend 2 bits (the llama.cpp TV-box / iPad
+  page weighs the two against each other in its speed-up table, the 2-bit
+  ternary layout of its section 18: 2-bit fields decode in fewer CPU
+  operations, base-3 digits take less memory).
 
 Readings taken (each listed in the design doc):
 

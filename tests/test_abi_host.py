@@ -46,7 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 @pytest.mark.parametrize("rows,cols,code", [(512, 512, 4), (14336, 4096, 4), (104, 1024, 3), (7, 256, 1),
-                                            (5, 384, 5), (4096, 14336, 2), (1, 128, 3)])
+                                            (5, 384, 5), (4096, 14336, 2), (1, 128, 3), (14336, 4096, 6),
+                                            (3, 640, 6), (1, 128, 6)])
 def test_pack_info_matches_oracle(lib, rows, cols, code):
     from bit_quantized_matmul_amd import binding
     assert binding.cq_pack_info(rows, cols, 128, code).as_dict() == ocq.pack_info(rows, cols, 128, code)
@@ -55,7 +56,8 @@ def test_pack_info_matches_oracle(lib, rows, cols, code):
 def test_pack_info_rejects_bad_arguments(lib):
     from bit_quantized_matmul_amd import binding
     lay = binding.CqLayout()
-    for args in [(4, 100, 128, 4), (4, 128, 128, 6), (0, 128, 128, 4), (4, 128, 96, 4), (4, 128, 128, 0)]:
+    for args in [(4, 100, 128, 4), (4, 128, 128, 7), (0, 128, 128, 4), (4, 128, 96, 4), (4, 128, 128, 0),
+                 (4, 100, 128, 6)]:
         assert lib.cq_pack_info(*args, ctypes.byref(lay)) == binding.BQM_EINVAL
     assert lib.cq_pack_info(4, 128, 128, 4, None) == binding.BQM_EINVAL
 
@@ -64,6 +66,7 @@ def test_analytic_levels_match_oracle(lib):
     from bit_quantized_matmul_amd import binding
     assert np.array_equal(binding.cq_analytic_levels(1), ocb.analytic_levels(1))
     assert np.array_equal(binding.cq_analytic_levels(5), ocb.analytic_levels(5))
+    assert np.array_equal(binding.cq_analytic_levels(6), ocb.analytic_levels(5))   # base-3: the ternary set
     out = (ctypes.c_float * 3)()
     assert lib.cq_analytic_levels(4, out) == binding.BQM_EINVAL
 
@@ -95,6 +98,15 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv_f32(p, ctypes.byref(big), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
+    # base-3 ternary: batch 1 only, no GEMM, the fused path needs the code buffers
+    t3 = binding.cq_pack_info(256, 512, 128, 6)
+    assert lib.cq_gemv(p, ctypes.byref(t3), cb, p, p, 1, p, None) == E.BQM_EINVAL      # analytic: NULL
+    assert lib.cq_gemv(p, ctypes.byref(t3), None, p, p, 2, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemm(p, ctypes.byref(t3), None, p, p, 4, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, None, None, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, ctypes.c_void_p(4100), p, None) == E.BQM_EALIGN
+    t3big = binding.cq_pack_info(8, 16512, 128, 6)                                      # 129 groups
+    assert lib.cq_gemv(p, ctypes.byref(t3big), None, p, p, 1, p, None) == E.BQM_ENOTSUP
     assert lib.q4_0_gemv(None, 4, 312, p, 1, p, None) == E.BQM_EINVAL
     assert lib.q4_0_gemv(p, 4, 312, p, 17, p, None) == E.BQM_ENOTSUP
     assert lib.q4_0_gemm(p, 4, 312, p, 0, p, None) == E.BQM_EINVAL

@@ -47,7 +47,7 @@ def levels(code, codebooks):
 
 
 def host_codebook(code, codebooks):
-    return None if code in (ocq.BINARY, ocq.TERNARY) else codebooks[code]
+    return None if code in (ocq.BINARY, ocq.TERNARY, ocq.TERNARY_B3) else codebooks[code]
 
 
 # ------------------------------------------------------------------ encoders
@@ -65,7 +65,7 @@ def test_act_quant_bit_exact(m, k):
     assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("code", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("code", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("rows,cols", [(300, 512), (3, 128), (65, 1024)])
 def test_cq_pack_bit_exact(code, rows, cols, codebooks):
     rng = np.random.default_rng(200 + code + rows)
@@ -181,6 +181,33 @@ def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     ref = omm.cq_reference(idx, n16, 128, code, lv, q_ref, s_ref)
     assert omm.rel_l2(y1, ref) <= TOL
+
+
+# Base-3 ternary, one token: one group slot a lane (up to 64 groups: 1, 3, 5, 32,
+# 64 groups, 64 / 16 / 8 / 2 / 1 rows a wave pass) and two (65, 112 and 128
+# groups), odd group counts (rows start 2 bytes off a word), ragged passes
+@pytest.mark.parametrize("rows,cols", [(300, 512), (5, 128), (1000, 384), (9, 640), (130, 4096),
+                                       (77, 8192), (33, 8320), (67, 14336), (50, 16384), (1, 256),
+                                       (257, 1152)])
+def test_cq_gemv_ternary_b3_parity(rows, cols, codebooks):
+    rng = np.random.default_rng(480 + rows + cols)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, ocq.TERNARY_B3, 1, codebooks)
+    ref = omm.cq_reference(idx, n16, 128, ocq.TERNARY_B3, lv, q, s)
+    lay = B.cq_pack_info(rows, cols, 128, ocq.TERNARY_B3)
+    y = host(B.cq_gemv(dev(blob), lay, None, dev(q), dev(s)))
+    err = omm.rel_l2(y, ref)
+    assert err <= TOL, f"rel L2 {err:.3e}"
+    # the same weights packed in 2-bit fields give the same product up to fp32 order
+    lay5 = B.cq_pack_info(rows, cols, 128, ocq.TERNARY)
+    y5 = host(B.cq_gemv(dev(ocq.make_blob(idx, n16, 128, ocq.TERNARY)), lay5, None, dev(q), dev(s)))
+    assert omm.rel_l2(y, y5) <= 1e-5
+    # fp32 activations: A8 into the code buffers, then the same product, bit for bit
+    x = inputs.activations(rng, 1, cols)
+    q_out = torch.empty((1, cols), dtype=torch.int8, device=DEV)
+    s_out = torch.empty((1,), dtype=torch.float32, device=DEV)
+    y1 = host(B.cq_gemv_f32(dev(blob), lay, None, dev(x), q_out=q_out, scale_out=s_out))
+    y2 = host(B.cq_gemv(dev(blob), lay, None, q_out, s_out))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
 @pytest.mark.parametrize("code", [1, 4, 5])
@@ -397,6 +424,28 @@ def test_full_size_bit_sweep_sampled(code, codebooks):
         y = host(B.cq_gemv(blob, lay, host_codebook(code, codebooks), q, s))
         ref = omm.cq_reference(idx[sel], n16[sel], 128, code, lv, host(q), host(s))
         assert omm.rel_l2(y[:, sel], ref) <= TOL, (code, batch)
+
+
+@pytest.mark.parametrize("rows,cols", [(14336, 4096), (4096, 14336)])
+def test_full_size_ternary_b3_sampled(rows, cols):
+    """Base-3 ternary at the sweep and down-projection shapes, one token, in
+    the launch the bench times: packed on the device (bit-exact on sampled
+    rows), product on sampled rows against the oracle."""
+    rng = np.random.default_rng(1100 + rows)
+    w = inputs.weight_matrix(rng, rows, cols, outliers=True)
+    code = ocq.TERNARY_B3
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    blob = B.cq_pack(dev(w), lay, None)
+    sel = sampled_rows(rng, rows, 32)
+    lv = levels(code, None)
+    idx, n16 = ocq.split_blob(host(blob), rows, cols, 128, code)
+    ridx, rn16 = ocq.encode(w[sel], 128, code, lv)
+    assert np.array_equal(idx[sel], ridx) and np.array_equal(n16[sel].view(np.uint16), rn16.view(np.uint16))
+    x = inputs.activations(rng, 1, cols)
+    q, s = B.act_fwht_quant_a8(dev(x))
+    y = host(B.cq_gemv(blob, lay, None, q, s))
+    ref = omm.cq_reference(idx[sel], n16[sel], 128, code, lv, host(q), host(s))
+    assert omm.rel_l2(y[:, sel], ref) <= TOL
 
 
 def test_full_size_minueza_pass():
