@@ -521,9 +521,22 @@ def bench_copy(torch, dev, steps):
 
 # -------------------------------------------------------------- cpu baseline
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(reps: int = 60, rows_per_matrix: int = 512):
-    """The oracle (unchanged) on a bounded sample of the decode step."""
-    from threadpoolctl import threadpool_info
+    """The oracle (unchanged) on a bounded sample of the decode step: the
+    plain definition (the reported value), the rotated-domain form, and the
+    plain definition on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from bit_quantized_matmul_amd import inputs
     from oracle import a8, codebook, cq, matmul
@@ -536,19 +549,34 @@ def cpu_baseline(reps: int = 60, rows_per_matrix: int = 512):
         idx, n16 = cq.encode(ws, 128, 4, lv)          # input preparation, not timed
         sample.append((idx, n16, x))
         nbytes += cq.pack_info(ws.shape[0], ws.shape[1], 128, 4)["idx_bytes"] + 2 * n16.size
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        for idx, n16, x in sample:
-            q, s = a8.act_quant_a8(x, 128, "fp32")
-            matmul.cq_reference(idx, n16, 128, 4, lv, q, s)
-    dt = time.perf_counter() - t0
+
+    def timed(product, n):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            for idx, n16, x in sample:
+                q, s = a8.act_quant_a8(x, 128, "fp32")
+                product(idx, n16, 128, 4, lv, q, s)
+        return time.perf_counter() - t0
+
+    dt = timed(matmul.cq_reference, reps)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    rot_reps = max(1, reps // 3)
+    dt_rot = timed(matmul.cq_rotated, rot_reps)
+    one_reps = max(1, reps // 10)
+    with threadpool_limits(limits=1):
+        dt_one = timed(matmul.cq_reference, one_reps)
     return dict(value=reps * nbytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
                 seconds=dt,
                 sample=f"first {rows_per_matrix} rows of each decode matrix (4096x4096, 1024x4096, "
                        f"14336x4096, 4096x14336), oracle A8 + plain-definition product "
                        f"(decode W_hat by FWHT, fp64 matmul), {reps} repetitions, "
-                       f"{nbytes} packed bytes per repetition")
+                       f"{nbytes} packed bytes per repetition",
+                rotated_domain=dict(value=rot_reps * nbytes / dt_rot / 1e9, seconds=dt_rot, reps=rot_reps,
+                                    cores=threads),
+                single_thread=dict(value=one_reps * nbytes / dt_one / 1e9, seconds=dt_one, reps=one_reps,
+                                   cores=1),
+                host=dict(cpu_count=os.cpu_count(), affinity=len(os.sched_getaffinity(0)),
+                          blas_threads=threads, model=cpu_model()))
 
 
 # ---------------------------------------------------------------------- main
