@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   auto kgroup = [&](int g) { const int x = g + rot; return g >= ng ? 0 : (x < ng ? x : x - ng); };
   u32x4 apre[kDepth][kAV];
   uint32_t bpre[kDepth][NB][IB], npre[N8 ? 1 : kDepth][NB];
-  u32x4 ncur[NB], nnext[NB];                       // N8: norms of this round's and the next round's groups
+  u32x4 ncur[NB], nnext[NB];                       // N8: norms of this loop round's groups and the next one's
   auto issue_norms = [&](int g0, u32x4 (&dst)[NB]) {
     const int gg = kgroup(g0);
 #pragma unroll
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     return o;
   };
   // group g's norm / 4 as an fp16 pair (scaling by 1/4 is exact): from
-  // prefetch slot d, or (N8) from this round's or the next round's norms,
+  // prefetch slot d, or (N8) from this loop round's or the next one's norms,
   // where group g is halfword g % 8
   auto take_group = [&](int g, int d, bool next) {
 #pragma unroll

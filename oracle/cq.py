@@ -19,7 +19,7 @@ mmap article's passage on the CQ format):
   ternary layout of its section 18: 2-bit fields decode in fewer CPU
   operations, base-3 digits take less memory).
 
-Readings taken (each listed in the design doc):
+Readings taken where the pages are silent or garbled:
 
 * Scale: the levels are on the N(0,1) scale, so the stored norm is the true
   L2 norm of the (normalized-H) rotated group and the quantized direction is

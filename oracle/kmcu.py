@@ -17,7 +17,7 @@ The Minueza-32M -> KMCU v1 page (pnsm.cn/news/1981961.html), section 4:
   that order); norms are f32, matrices Q4_0 (section 1: --force-tie keeps
   no separate output head).
 
-Readings (listed in the design doc): the directory follows the header directly
+Readings where the page leaves freedom: the directory follows the header directly
 (dir_offset = 128) and the data the directory (data_offset = the first
 64-byte boundary after it); unused header and record bytes are zero.
 """

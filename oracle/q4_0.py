@@ -10,7 +10,7 @@ The Minueza-32M -> KMCU v1 page (pnsm.cn/news/1981961.html):
   quantizing, so a block never straddles two rows; block id = r*nblk + b
   with nblk = ceil(cols/32).
 
-Readings of the page's garbled numpy (listed in the design doc): d is 1.0 for an
+Readings of the page's garbled numpy: d is 1.0 for an
 all-zero block (``amax > 0`` in the comparison that lost its operator);
 codes are computed with the fp32 d, the block stores fp16(d) (half-even) and
 decodes with it; rint is half-to-even; the division is fp32, correctly
