@@ -19,7 +19,7 @@ bit-width sweep, the same decode layer shapes at 4 and
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|copy   (profiling runs)
+       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|floor|copy   (profiling runs)
 """
 from __future__ import annotations
 
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "q4_0_prefill", "sweep",
-                                       "batched", "kmcu", "copy"])
+                                       "batched", "kmcu", "floor", "copy"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -263,6 +263,26 @@ def bench_dominant(B, torch, dev, cbs, steps, mats=None, pool=None):
     return dict(kernel="cq_gemv_kernel, fused A8 (cq_gemv_f32: CQ 4-bit GEMV, 4096x14336, batch 1)",
                 avg_us=d_ms * 1e3, launches=n * reps, algo_bytes=algo,
                 achieved_gbps=algo / d_ms / 1e6)
+
+
+def bench_read_floor(torch, dev, rows: int = 4096, cols: int = 1852):
+    """Vendor kernels reading about the dominant kernel's bytes (4096 x 1852
+    fp32 = 30.3 MB, against the 4096x14336 GEMV's 30.35 MB), HBM-cold (cycling
+    >= 1 GiB of buffers), timed like the GEMV: torch's row sums (the fastest
+    plain streaming read found among torch's reductions) and torch's fp32
+    GEMV; and a trivial kernel, the launch floor of any one launch."""
+    nbytes = rows * cols * 4
+    n = pool_copies(nbytes)
+    pool = [torch.zeros((rows, cols), dtype=torch.float32, device=dev) for _ in range(n)]
+    v = torch.zeros(cols, dtype=torch.float32, device=dev)
+    d_sum = graph_mean_ms(torch, [(lambda k=k: pool[k].sum(dim=1)) for k in range(n)])
+    d_mv = graph_mean_ms(torch, [(lambda k=k: torch.mv(pool[k], v)) for k in range(n)])
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    e = graph_mean_ms(torch, [tiny.zero_ for _ in range(64)])
+    del pool
+    torch.cuda.empty_cache()
+    rate = lambda d: dict(us=d * 1e3, gbps=nbytes / d / 1e6, frac=nbytes / d / 1e6 / HBM_PEAK_GBPS)
+    return dict(bytes=nbytes, row_sums=rate(d_sum), fp32_gemv_torch_mv=rate(d_mv), empty_launch_us=e * 1e3)
 
 
 def bench_prefill(B, torch, dev, cbs, steps, warmup):
@@ -623,6 +643,9 @@ def main():
     if args.only == "kmcu":
         print(json.dumps(bench_kmcu_load(B, torch, dev, args.steps)))
         return
+    if args.only == "floor":
+        print(json.dumps(bench_read_floor(torch, dev)))
+        return
     cbs = fit_codebooks(B, torch, dev)
     log("codebooks fitted on device")
     if args.only == "dominant":
@@ -664,6 +687,9 @@ def main():
     bat = bench_batched(B, torch, dev, cbs, args.steps)
     log(f"batched decode step: 4 tokens {bat['step_b4']['us']:.1f} us, "
         f"16 tokens {bat['step_b16']['us']:.1f} us")
+    floor = bench_read_floor(torch, dev)
+    log(f"30 MB vendor reads: row sums {floor['row_sums']['us']:.2f} us, fp32 mv {floor['fp32_gemv_torch_mv']['us']:.2f} us, "
+        f"empty launch {floor['empty_launch_us']:.2f} us")
     km = bench_kmcu_load(B, torch, dev, args.steps)
     log(f"kmcu load: {km['file_mib']:.2f} MiB image, pinned {km['pinned_gbps']:.1f} GB/s, "
         f"pageable {km['pageable_gbps']:.1f} GB/s")
@@ -718,6 +744,7 @@ def main():
         "bit_sweep_14336x4096": sweep,
         "batched_decode_cb4": bat,
         "kmcu_load_minueza_tied": km,
+        "hbm_read_floor_30MB": floor,
     }
     print(json.dumps(line))
 
