@@ -307,6 +307,17 @@ def bench_prefill(B, torch, dev, cbs, steps, warmup):
         tf = flops / ms / 1e9
         out[label] = dict(m=int(q.shape[0]), us=ms * 1e3, tflops=tf, frac=tf / MFMA_F16_PEAK_TFLOPS)
         del blob, y
+    # context: the dense fp16 GEMM the format avoids (hipBLASLt via torch.mm,
+    # contiguous [M, K] x [K, N] operands, fp16 weights of the same shape)
+    m = q.shape[0]
+    for label, w in wl.weights:
+        rows, cols = w.shape
+        a16 = x.to(torch.float16)
+        wt16 = torch.from_numpy(w).to(dev).to(torch.float16).t().contiguous()
+        d = graph_mean_ms(torch, [(lambda: torch.mm(a16, wt16)) for _ in range(20)])
+        tf = 2.0 * m * rows * cols / d / 1e9
+        out[f"dense_fp16_torch_mm_{label}"] = dict(m=int(m), us=d * 1e3, tflops=tf, frac=tf / MFMA_F16_PEAK_TFLOPS)
+        del wt16
     # A8 on the 512 x 4096 prefill activations
     for _ in range(warmup):
         B.act_fwht_quant_a8(x, q=q, scale=s)
