@@ -6,9 +6,11 @@
 // dot(w_g, x_g) = norm_g/G * dot(cb[idx_g], H_u x_g): the activation is
 // rotated once here and the weights are never transformed back.
 //
-// One workgroup per token row.  Each lane owns 8 consecutive elements of a
-// 128-wide group; 16 lanes hold one group.  Butterfly stages of half-width
-// 1, 2, 4 are inside a lane, 8..64 across lanes (partner lane = lane ^ (h/8)).
+// One workgroup per token row, as many threads as the row has 8-element
+// chunks (a multiple of 64, at most 1024).  Each lane owns 8 consecutive
+// elements of a 128-wide group; 16 lanes hold one group.  Butterfly stages of
+// half-width 1, 2, 4 are inside a lane, 8..64 across lanes (partner lane =
+// lane ^ (h/8)), exchanged with DPP moves within each 16-lane row.
 // Every stage computes (a+b, a-b) for the pair (j, j+h), j the lower index,
 // in fp32, so the result is bit-identical to any fp32 evaluation of the same
 // network.  Then s = max|u| / 127 over the row (1 for a zero row) and
@@ -18,7 +20,7 @@
 namespace bqm {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kMaxThreads = 1024;
 constexpr int kPerLane = 8;
 constexpr int kMaxChunksPerThread = 8;    // k <= 1024 * 8 * 8 = 65536
 
@@ -40,11 +42,36 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return v;
 }
 
+// The partner lane of the cross-lane stages (lane ^ 1, ^ 2, ^ 4, ^ 8 inside
+// a 16-lane row), read with DPP: quad permutations for 1 and 2, the half-row
+// mirror then the quad reversal for 4, a rotation by 8 within the row for 8.
+template <int HL>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (HL == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  if constexpr (HL == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+  if constexpr (HL == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, true);
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
+  }
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+}
+
+template <int HL, int CPT>
+__device__ __forceinline__ void cross_stage(float (&v)[CPT][8], int c, int lane) {
+  const bool upper = (lane & HL) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = xor_lane<HL>(v[c][e]);
+    v[c][e] = upper ? (other - v[c][e]) : (v[c][e] + other);
+  }
+}
+
 // u / s with IEEE round-to-nearest-even (HIP's default fp32 division is
 // correctly rounded; spelled out so the intent survives compiler flags).
 __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
 
-template <int CPT>
+template <int CPT, int kThreads>
 __global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
     const float *__restrict__ x, int k, int8_t *__restrict__ q, float *__restrict__ scale) {
   const int row = blockIdx.x;
@@ -83,15 +110,10 @@ __global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
     // Chunks with ci >= chunks belong to whole groups past the row end (k is a
     // multiple of 128 and 16 lanes hold one group), so their lanes exchange
     // only with each other.
-#pragma unroll
-    for (int hl = 1; hl < 16; hl <<= 1) {
-      const bool upper = (lane & hl) != 0;
-#pragma unroll
-      for (int e = 0; e < kPerLane; ++e) {
-        const float other = __shfl_xor(v[c][e], hl, 64);
-        v[c][e] = upper ? (other - v[c][e]) : (v[c][e] + other);
-      }
-    }
+    cross_stage<1>(v, c, lane);
+    cross_stage<2>(v, c, lane);
+    cross_stage<4>(v, c, lane);
+    cross_stage<8>(v, c, lane);
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
   }
@@ -134,17 +156,21 @@ __global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
 
 hipError_t launch_act_fwht_quant_a8(const float *x, int m, int k, int8_t *q, float *scale,
                                     hipStream_t s) {
-  const int chunks = k / kPerLane;
-  const int cpt = (chunks + kThreads - 1) / kThreads;
-  dim3 grid(m), block(kThreads);
-  if (cpt <= 1)
-    act_fwht_quant_a8_kernel<1><<<grid, block, 0, s>>>(x, k, q, scale);
-  else if (cpt <= 2)
-    act_fwht_quant_a8_kernel<2><<<grid, block, 0, s>>>(x, k, q, scale);
-  else if (cpt <= 4)
-    act_fwht_quant_a8_kernel<4><<<grid, block, 0, s>>>(x, k, q, scale);
+  const int chunks = k / kPerLane;               // a multiple of 16 (k % 128 == 0)
+  const dim3 grid(m);
+  // one chunk a thread up to 1024 chunks (threads rounded up to whole waves)
+  if (chunks <= 64) act_fwht_quant_a8_kernel<1, 64><<<grid, 64, 0, s>>>(x, k, q, scale);
+  else if (chunks <= 128) act_fwht_quant_a8_kernel<1, 128><<<grid, 128, 0, s>>>(x, k, q, scale);
+  else if (chunks <= 256) act_fwht_quant_a8_kernel<1, 256><<<grid, 256, 0, s>>>(x, k, q, scale);
+  else if (chunks <= 512) act_fwht_quant_a8_kernel<1, 512><<<grid, 512, 0, s>>>(x, k, q, scale);
+  else if (chunks <= kMaxThreads)
+    act_fwht_quant_a8_kernel<1, kMaxThreads><<<grid, kMaxThreads, 0, s>>>(x, k, q, scale);
+  else if (chunks <= 2 * kMaxThreads)
+    act_fwht_quant_a8_kernel<2, kMaxThreads><<<grid, kMaxThreads, 0, s>>>(x, k, q, scale);
+  else if (chunks <= 4 * kMaxThreads)
+    act_fwht_quant_a8_kernel<4, kMaxThreads><<<grid, kMaxThreads, 0, s>>>(x, k, q, scale);
   else
-    act_fwht_quant_a8_kernel<kMaxChunksPerThread><<<grid, block, 0, s>>>(x, k, q, scale);
+    act_fwht_quant_a8_kernel<kMaxChunksPerThread, kMaxThreads><<<grid, kMaxThreads, 0, s>>>(x, k, q, scale);
   return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ def host_codebook(code, codebooks):
 
 # ------------------------------------------------------------------ encoders
 
-@pytest.mark.parametrize("m,k", [(1, 128), (3, 512), (5, 4096), (2, 14336), (1, 65536)])
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 512), (2, 1024), (4, 2048), (5, 4096), (3, 8192), (2, 14336),
+                                 (2, 24576), (1, 65536), (512, 4096)])
 def test_act_quant_bit_exact(m, k):
     rng = np.random.default_rng(100 + m + k)
     x = inputs.activations(rng, m, k)
