@@ -323,3 +323,26 @@ def test_load_whole_image_in_one_copy():
             assert view.data_ptr() % 64 == 0
             raw = np.frombuffer(buf, np.uint8, r["nbytes"], r["offset"])
             assert np.array_equal(view.cpu().numpy(), raw), r["name"]
+
+
+def test_abi_edge_cases_empty_file_and_full_length_name():
+    """A file with no tensors parses (and its empty data region uploads as a
+    no-op before any device call); a name of exactly 24 bytes has no NUL in
+    the record and still comes back whole."""
+    import ctypes
+    B = lib()
+    L = B.load_library()
+    empty = ok.write(ok.MINUEZA_CONFIG, [])
+    h = B.kmcu_header(empty)
+    assert (h.n_tensors, h.dir_offset, h.data_offset) == (0, 128, 128) and len(empty) == 128
+    assert _status(lambda: B.kmcu_tensor(empty, 0)) == EINVAL
+    assert _status(lambda: B.kmcu_find(empty, "tok_embed")) == EINVAL
+    arr = np.frombuffer(empty, np.uint8)
+    assert L.kmcu_upload_data(ctypes.c_void_p(arr.ctypes.data), arr.nbytes, ctypes.c_void_p(4096), 0, None) == 0
+    name = "x" * 24
+    buf = ok.write(ok.MINUEZA_CONFIG, [(name, ok.F32, 2, 3, np.arange(6, dtype="<f4").tobytes())])
+    t = B.kmcu_find(buf, name)
+    assert t.name.decode() == name and (t.n_rows, t.n_cols, t.nbytes) == (2, 3, 24)
+    assert _status(lambda: B.kmcu_find(buf, name + "y")) == EINVAL       # 25 bytes never match
+    from bit_quantized_matmul_amd import kmcu as pk
+    assert bytes(pk.write(ok.MINUEZA_CONFIG, [(name, ok.F32, 2, 3, np.arange(6, dtype="<f4").tobytes())])) == buf
