@@ -15,7 +15,9 @@
 //  * A lane owns SL (1 or 2) group slots, groups li and li + P, for every row
 //    it visits; a row takes P lanes (P a power of two, P * SL >= groups) and
 //    a wave holds 64 / P rows at a time.  The lane's activations never change,
-//    so they sit in registers, rearranged once: for weight byte j, the int8
+//    so they sit in registers, rearranged once (read from a copy of the
+//    token's codes that the workgroup stages in LDS, 144 bytes a group so that
+//    16 lanes reading 16 groups hit distinct banks): for weight byte j, the int8
 //    codes at positions 5j .. 5j+3 as one dword, and the code at 5j+4 in
 //    byte j % 4 of dword j / 4 of a second set (7 dwords a group).
 //  * A weight byte's five digits come from an LDS table: entry v holds
@@ -26,7 +28,7 @@
 //    to build for every workgroup.
 //  * A lane's 26 group bytes start 2-byte aligned: they come as the 32 bytes
 //    from the 4-byte-aligned address below them, realigned with v_alignbyte.
-//  * Rows are walked two passes at a time, the next pass's loads (the two
+//  * A wave walks at least two passes, the next pass's loads (the two
 //    16-byte windows and the norm of each slot) in flight while one computes;
 //    every load is unconditional (past the end: offset 0x80000000, zeros).
 #include "bqm_common.h"
@@ -39,6 +41,8 @@ constexpr int kT3Copies = 16;                      // table copies
 constexpr int kT3Entries = 256;                    // every byte value (243.. are not digits: zeros)
 constexpr int kT3TableBytes = kT3Entries * kT3Copies * 8;   // 32 KB
 constexpr uint32_t kT3OOB = 0x80000000u;
+constexpr int kT3MaxGroups = 128;                  // cols <= 16384
+constexpr int kT3QStride = kGroup + 16;            // bytes a group in the LDS copy of the codes
 typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_t3(const void *base, uint32_t bytes) {
@@ -58,6 +62,7 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     uint32_t norm_bytes, const int8_t *__restrict__ q, const float *__restrict__ scale,
     float *__restrict__ y, int rows, int ng, int plog2, int passes_per_wave, float cfac) {
   __shared__ __align__(16) uint8_t tab[kT3TableBytes];
+  __shared__ __align__(16) uint8_t qlds[kT3MaxGroups * kT3QStride];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int P = 1 << plog2;
@@ -86,6 +91,14 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     for (int c = 0; c < kT3Copies / 4; ++c) row[c] = make_uint4(lo, hi, lo, hi);
   }
 
+  // the token's codes into LDS, 16 bytes a thread per step
+  for (int c = t; c < ng * (kGroup / 16); c += kT3Threads) {
+    const int g = c >> 3, w = c & 7;
+    *reinterpret_cast<u32x4t *>(qlds + g * kT3QStride + 16 * w) =
+        *reinterpret_cast<const u32x4t *>(q + (size_t)c * 16);
+  }
+  __syncthreads();
+
   // the lane's activations per slot, five positions per weight byte
   constexpr int kQB = (kTritBytes + 3) / 4;
   uint32_t qa[SL][kTritBytes], qb[SL][kQB];
@@ -94,7 +107,7 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     const int g = li + P * s;
     uint32_t qw[kGroup / 4 + 1];
     if (g < ng) {
-      const u32x4t *src = reinterpret_cast<const u32x4t *>(q + (size_t)g * kGroup);
+      const u32x4t *src = reinterpret_cast<const u32x4t *>(qlds + g * kT3QStride);
 #pragma unroll
       for (int i = 0; i < kGroup / 16; ++i) {
         const u32x4t v = src[i];
@@ -115,7 +128,6 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
       qb[s][j >> 2] |= ((qw[p4 >> 2] >> (8 * (p4 & 3))) & 0xFFu) << (8 * (j & 3));
     }
   }
-  __syncthreads();
 
   // the whole blob: a group's 32-byte window can reach 6 bytes past the
   // indices, into the padding and norms that follow them
@@ -213,8 +225,9 @@ hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const 
   const int rpp = 64 >> plog2;
   const long passes = ((long)L.rows + rpp - 1) / rpp;
   const long waves_max = (long)num_cus * 2 * (kT3Threads / kWave);
-  // at least 4 passes a wave, so its activation set-up is not repeated per row
-  const long waves = (passes + 3) / 4 < waves_max ? (passes + 3) / 4 : waves_max;
+  // at least 2 passes a wave (its activation set-up is not repeated per row),
+  // as many waves as that gives up to two workgroups a CU
+  const long waves = (passes + 1) / 2 < waves_max ? (passes + 1) / 2 : waves_max;
   const int per_wave = (int)((passes + waves - 1) / waves);
   const long used = (passes + per_wave - 1) / per_wave;          // waves with work
   const int blocks = (int)((used + (kT3Threads / kWave) - 1) / (kT3Threads / kWave));
