@@ -358,12 +358,10 @@ def bench_q4_0(B, torch, dev, steps, warmup):
     for _ in range(steps):
         one_pass()
     ms_eager = t.stop_ms() / steps
-    # the tied head alone (the only matrix large enough to be bandwidth-bound)
+    # the tied head alone (the only matrix large enough to be bandwidth-bound),
+    # graph-timed: eager launches from Python are host-bound at this size
     rows, cols, blocks, x, y = items[-1]
-    t.start()
-    for _ in range(steps):
-        B.q4_0_gemv(blocks, rows, cols, x, y=y)
-    ms_head = t.stop_ms() / steps
+    ms_head = graph_mean_ms(torch, [(lambda: B.q4_0_gemv(blocks, rows, cols, x, y=y)) for _ in range(max(steps, 20))])
     return dict(launches=len(items), bytes=total, us_graph=ms * 1e3, gbps_graph=total / ms / 1e6,
                 us_eager=ms_eager * 1e3, head_us=ms_head * 1e3,
                 head_gbps=blocks.numel() / ms_head / 1e6, note="weights in Infinity Cache (13 MB pass)")
