@@ -96,6 +96,10 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv(ctypes.c_void_p(4097), ctypes.byref(lay), cb, p, p, 1, p, None) == E.BQM_EALIGN
     big = binding.cq_pack_info(8, 32768, 128, 4)
     assert lib.cq_gemv_f32(p, ctypes.byref(big), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
+    over = binding.cq_pack_info(8, 16512, 128, 4)                      # one group past the fused limit
+    assert lib.cq_gemv_f32(p, ctypes.byref(over), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
+    wide = binding.cq_pack_info(8, 36992, 128, 4)                      # one group past the int8 limit
+    assert lib.cq_gemv(p, ctypes.byref(wide), cb, p, p, 1, p, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
     # base-3 ternary: batch 1 only, no GEMM, the fused path needs the code buffers

@@ -328,6 +328,30 @@ def test_graph_replays_match_eager(codebooks):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}, output {i}"
 
 
+# the largest rows each path takes: the int8 GEMV up to 36864 columns (its fp16
+# copy of one token fills the 72 KB of LDS; several tokens go one a launch),
+# the fused fp32 GEMV up to 16384, the GEMM with a long K
+@pytest.mark.parametrize("code", [1, 4])
+@pytest.mark.parametrize("entry,rows,cols,batch", [("gemv", 33, 36864, 1), ("gemv", 20, 36864, 3),
+                                                   ("f32", 9, 16384, 1), ("f32", 9, 16384, 4),
+                                                   ("gemm", 100, 36864, 64)])
+def test_maximum_sizes(code, entry, rows, cols, batch, codebooks):
+    rng = np.random.default_rng(980 + code + rows + batch)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, batch, codebooks)
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    cb = host_codebook(code, codebooks)
+    if entry == "f32":
+        x = inputs.activations(rng, batch, cols)
+        q, s = oa8.act_quant_a8(x, 128, "fp32")
+        y = host(B.cq_gemv_f32(dev(blob), lay, cb, dev(x)))
+    elif entry == "gemv":
+        y = host(B.cq_gemv(dev(blob), lay, cb, dev(q), dev(s)))
+    else:
+        y = host(B.cq_gemm(dev(blob), lay, cb, dev(q), dev(s)))
+    ref = omm.cq_reference(idx, n16, 128, code, lv, q, s)
+    assert omm.rel_l2(y, ref) <= TOL
+
+
 def test_results_are_deterministic(codebooks):
     rng = np.random.default_rng(700)
     lv, idx, n16, blob, q, s = oracle_case(rng, 300, 1024, 4, 40, codebooks)
