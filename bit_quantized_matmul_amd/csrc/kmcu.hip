@@ -120,7 +120,9 @@ int kmcu_find(const void *file, uint64_t size, const char *name, bqm_kmcu_tensor
 int kmcu_upload(const void *file, uint64_t size, const bqm_kmcu_tensor *t, void *dst,
                 bqm_stream_t stream) {
   if (!file || !t || !dst) return BQM_EINVAL;
-  if ((uint64_t)t->offset + t->nbytes > size || t->offset % kAlign != 0 ||
+  // the record may come from the caller: the same checks as kmcu_tensor's
+  if ((t->dtype != BQM_KMCU_F32 && t->dtype != BQM_KMCU_Q4) || t->n_rows == 0 || t->n_cols == 0 ||
+      (uint64_t)t->offset + t->nbytes > size || t->offset % kAlign != 0 ||
       t->nbytes != payload_bytes(t->dtype, t->n_rows, t->n_cols))
     return BQM_EINVAL;
   if (((uintptr_t)dst & 15u) != 0) return BQM_EALIGN;

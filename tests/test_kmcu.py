@@ -231,6 +231,10 @@ def test_abi_upload_rejects_bad_arguments_before_any_copy(small):
     assert L.kmcu_upload(p, n, ctypes.byref(t), None, None) == EINVAL
     assert L.kmcu_upload(p, n, None, ctypes.c_void_p(4096), None) == EINVAL
     assert L.kmcu_upload(p, n, ctypes.byref(t), ctypes.c_void_p(4096 + 8), None) == EALIGN
+    for field, value in (("dtype", 3), ("n_rows", 0)):
+        bad = B.KmcuTensor.from_buffer_copy(t)
+        setattr(bad, field, value)
+        assert L.kmcu_upload(p, n, ctypes.byref(bad), ctypes.c_void_p(4096), None) == EINVAL, field
     short = B.KmcuTensor.from_buffer_copy(t)
     short.nbytes -= 18
     assert L.kmcu_upload(p, n, ctypes.byref(short), ctypes.c_void_p(4096), None) == EINVAL
