@@ -35,6 +35,92 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// One lane's block: the 16 bytes from the 4-byte-aligned address below it and
+// the next 4 (2 for a block that ends the buffer); ok == false reads zeros.
+struct BlockLoad {
+  uint4 v;
+  uint32_t v4, sh;
+};
+
+__device__ __forceinline__ BlockLoad load_block(__amdgpu_buffer_rsrc_t rw, bool ok, uint32_t off,
+                                                uint32_t total) {
+  BlockLoad L;
+  const uint32_t a4 = off & ~3u;
+  L.sh = ok ? (off & 3u) : 0u;                     // 0 or 2: blocks are 2-byte aligned
+  L.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? a4 : kOOB, 0, 0));
+  const bool w4 = ok && a4 + 20 <= total;          // the 4 bytes after exist
+  const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rw, w4 ? a4 + 16 : kOOB, 0, 0);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (ok && !w4) ? a4 + 16 : kOOB, 0, 0);
+  L.v4 = lo | hi;
+  return L;
+}
+
+// acc[b] += d * sum_{j<32} (nib_j - 8) * x[b][e0 + j] for the loaded block,
+// x from the LDS copy xs (row stride XS floats).
+template <int BATCH, int XS>
+__device__ __forceinline__ void block_dot(const BlockLoad &L, const float (*xs)[XS], int e0,
+                                          float (&acc)[BATCH]) {
+  uint32_t w0, w1, w2, w3, w4;
+  if (L.sh == 0) {
+    w0 = L.v.x; w1 = L.v.y; w2 = L.v.z; w3 = L.v.w; w4 = L.v4;
+  } else {
+    w0 = __builtin_amdgcn_alignbyte(L.v.y, L.v.x, 2);
+    w1 = __builtin_amdgcn_alignbyte(L.v.z, L.v.y, 2);
+    w2 = __builtin_amdgcn_alignbyte(L.v.w, L.v.z, 2);
+    w3 = __builtin_amdgcn_alignbyte(L.v4, L.v.w, 2);
+    w4 = L.v4 >> 16;
+  }
+  const float d = half_bits_to_float((uint16_t)(w0 & 0xFFFFu));
+  uint32_t nib[4];                                 // byte k of nib[w]: elements 8w+2k (low), 8w+2k+1 (high)
+  nib[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
+  nib[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
+  nib[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
+  nib[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 xa = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w]);
+      const float4 xc = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w + 4]);
+      const uint32_t lo = nib[w] & 0x0F0F0F0Fu;
+      const uint32_t hi = (nib[w] >> 4) & 0x0F0F0F0Fu;
+      s0 = fmaf(ubyte_f<0>(lo) - 8.0f, xa.x, s0);
+      s1 = fmaf(ubyte_f<0>(hi) - 8.0f, xa.y, s1);
+      s0 = fmaf(ubyte_f<1>(lo) - 8.0f, xa.z, s0);
+      s1 = fmaf(ubyte_f<1>(hi) - 8.0f, xa.w, s1);
+      s0 = fmaf(ubyte_f<2>(lo) - 8.0f, xc.x, s0);
+      s1 = fmaf(ubyte_f<2>(hi) - 8.0f, xc.y, s1);
+      s0 = fmaf(ubyte_f<3>(lo) - 8.0f, xc.z, s0);
+      s1 = fmaf(ubyte_f<3>(hi) - 8.0f, xc.w, s1);
+    }
+    acc[b] = fmaf(d, s0 + s1, acc[b]);
+  }
+}
+
+// x [BATCH, cols] columns [col0, col0 + n) to xs, zeros past cols.
+template <int BATCH, int XS>
+__device__ __forceinline__ void stage_x(const float *__restrict__ x, int cols, int col0, bool vec,
+                                        float (*xs)[XS]) {
+  const int ncol = min(XS, cols - col0);
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    const float *xb = x + (size_t)b * cols + col0;
+    for (int e = threadIdx.x * 4; e < XS; e += kThreads * 4) {
+      float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (vec && e + 3 < ncol) {
+        q = *reinterpret_cast<const float4 *>(xb + e);
+      } else {
+        if (e < ncol) q.x = xb[e];
+        if (e + 1 < ncol) q.y = xb[e + 1];
+        if (e + 2 < ncol) q.z = xb[e + 2];
+        if (e + 3 < ncol) q.w = xb[e + 3];
+      }
+      *reinterpret_cast<float4 *>(&xs[b][e]) = q;
+    }
+  }
+}
+
 template <int BATCH, int P>
 __global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
     const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t total,
@@ -53,83 +139,14 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
   for (int b = 0; b < BATCH; ++b) acc[b] = 0.0f;
   for (int c0 = 0; c0 < nblk; c0 += kChunk) {
     // the lane's block c0 + j: its loads first (out of range reads 0)
-    uint4 v[1];
-    uint32_t v4[1], sh[1];
-    {
-      const int i = 0;
-      const int blk = c0 + j;
-      const bool ok = rok && blk < nblk;
-      const uint32_t off = ok ? (uint32_t)(((size_t)row * nblk + blk) * kBlockBytes) : 0u;
-      const uint32_t a4 = off & ~3u;
-      sh[i] = off & 3u;                                    // 0 or 2: blocks are 2-byte aligned
-      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? a4 : kOOB, 0, 0));
-      const bool w4 = ok && a4 + 20 <= total;              // the 4 bytes after exist
-      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rw, w4 ? a4 + 16 : kOOB, 0, 0);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (ok && !w4) ? a4 + 16 : kOOB, 0, 0);
-      v4[i] = lo | hi;
-    }
-    // x columns [32 c0, 32 (c0 + P)) to LDS, zero past cols
-    const int col0 = c0 * kBlock;
-    const int ncol = min(kChunk * kBlock, cols - col0);
+    const int blk = c0 + j;
+    const bool ok = rok && blk < nblk;
+    const BlockLoad L = load_block(rw, ok, ok ? (uint32_t)(((size_t)row * nblk + blk) * kBlockBytes) : 0u, total);
+    // x columns [32 c0, 32 (c0 + P)) to LDS meanwhile, zero past cols
     if (c0 > 0) __syncthreads();                           // the previous chunk's reads are done
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const float *xb = x + (size_t)b * cols + col0;
-#pragma unroll
-      for (int e = t * 4; e < kChunk * kBlock; e += kThreads * 4) {
-        float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (vec && e + 3 < ncol) {
-          q = *reinterpret_cast<const float4 *>(xb + e);
-        } else {
-          if (e < ncol) q.x = xb[e];
-          if (e + 1 < ncol) q.y = xb[e + 1];
-          if (e + 2 < ncol) q.z = xb[e + 2];
-          if (e + 3 < ncol) q.w = xb[e + 3];
-        }
-        *reinterpret_cast<float4 *>(&xs[b][e]) = q;
-      }
-    }
+    stage_x<BATCH>(x, cols, c0 * kBlock, vec, xs);
     __syncthreads();
-    {
-      const int i = 0;
-      uint32_t w0, w1, w2, w3, w4;
-      if (sh[i] == 0) {
-        w0 = v[i].x; w1 = v[i].y; w2 = v[i].z; w3 = v[i].w; w4 = v4[i];
-      } else {
-        w0 = __builtin_amdgcn_alignbyte(v[i].y, v[i].x, 2);
-        w1 = __builtin_amdgcn_alignbyte(v[i].z, v[i].y, 2);
-        w2 = __builtin_amdgcn_alignbyte(v[i].w, v[i].z, 2);
-        w3 = __builtin_amdgcn_alignbyte(v4[i], v[i].w, 2);
-        w4 = v4[i] >> 16;
-      }
-      const float d = half_bits_to_float((uint16_t)(w0 & 0xFFFFu));
-      uint32_t nib[4];                                     // byte k of nib[w]: elements 8w+2k (low), 8w+2k+1 (high)
-      nib[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
-      nib[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
-      nib[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
-      nib[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
-      const int e0 = j * kBlock;                           // column of the block within the chunk
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float4 xa = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w]);
-          const float4 xc = *reinterpret_cast<const float4 *>(&xs[b][e0 + 8 * w + 4]);
-          const uint32_t lo = nib[w] & 0x0F0F0F0Fu;
-          const uint32_t hi = (nib[w] >> 4) & 0x0F0F0F0Fu;
-          s0 = fmaf(ubyte_f<0>(lo) - 8.0f, xa.x, s0);
-          s1 = fmaf(ubyte_f<0>(hi) - 8.0f, xa.y, s1);
-          s0 = fmaf(ubyte_f<1>(lo) - 8.0f, xa.z, s0);
-          s1 = fmaf(ubyte_f<1>(hi) - 8.0f, xa.w, s1);
-          s0 = fmaf(ubyte_f<2>(lo) - 8.0f, xc.x, s0);
-          s1 = fmaf(ubyte_f<2>(hi) - 8.0f, xc.y, s1);
-          s0 = fmaf(ubyte_f<3>(lo) - 8.0f, xc.z, s0);
-          s1 = fmaf(ubyte_f<3>(hi) - 8.0f, xc.w, s1);
-        }
-        acc[b] = fmaf(d, s0 + s1, acc[b]);
-      }
-    }
+    block_dot<BATCH>(L, xs, j * kBlock, acc);
   }
   // butterfly over the P lanes of the row (a fixed order: deterministic)
 #pragma unroll
