@@ -13,9 +13,10 @@
  *     been synchronized.  Calls that share buffers must be ordered by the
  *     caller (same stream or events).
  *   - Every argument is validated on the host before anything is launched.
- *     The return value is BQM_OK (0) or a negative BQM_E* code; on error
- *     nothing has been enqueued.  BQM_EDEVICE reports a HIP error seen while
- *     launching (hipGetLastError).
+ *     The return value is BQM_OK (0) or a negative BQM_E* code; after a
+ *     validation error nothing has been enqueued.  BQM_EDEVICE reports a HIP
+ *     error seen while launching (hipGetLastError); a call made of two
+ *     launches may then have enqueued the first.
  *   - Matrices are row-major.  Weight matrices are [out, in] = [rows, cols]:
  *     every output row is contiguous along the reduction axis and quant
  *     groups run along that axis ("14MB holds 45M parameters: dissecting
@@ -105,7 +106,7 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * blob [device] packed as `layout` [host] describes (16-byte aligned);
  * codebook [host] `layout->levels` fp32 values for bits 2/3/4, index order
  * (each finite and bfloat16-representable, hence exact in fp16 too;
- * BQM_EINVAL otherwise), NULL for bits 1 and 5; q [device] int8 [batch, cols] from act_fwht_quant_a8;
+ * BQM_EINVAL otherwise), NULL for bits 1, 5 and 6; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
  * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch >= 2
  * (>= 3 when cols > 4096) and cols <= 16384 the product runs on the matrix
