@@ -486,8 +486,6 @@ def bench_sweep(B, torch, dev, cbs, steps):
         pool = [blob] + [blob.clone() for _ in range(n - 1)]
         for a in acts:
             batch = a.shape[0]
-            if code == 6 and batch > 1:                # base-3 ternary: one token only
-                continue
             q, s = B.act_fwht_quant_a8(a)
             y = torch.empty((batch, rows), dtype=torch.float32, device=dev)
             d = graph_mean_ms(torch, [

@@ -211,7 +211,8 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   rc = current_device(&cus);
   if (rc) return rc;
   if (base3)
-    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q, scale, y, cus, (hipStream_t)stream));
+    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
+                                       (hipStream_t)stream));
   return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
                                   (hipStream_t)stream));
 }
@@ -238,9 +239,9 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
   rc = current_device(&cus);
   if (rc) return rc;
   if (base3) {
-    const hipError_t e = launch_act_fwht_quant_a8(x, 1, layout->cols, q_out, scale_out, (hipStream_t)stream);
+    const hipError_t e = launch_act_fwht_quant_a8(x, batch, layout->cols, q_out, scale_out, (hipStream_t)stream);
     if (e != hipSuccess) return BQM_EDEVICE;
-    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q_out, scale_out, y, cus,
+    return status_of(launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q_out, scale_out, batch, y, cus,
                                        (hipStream_t)stream));
   }
   return status_of(launch_cq_gemv_f32((const uint8_t *)blob, *layout, T, x, batch, y, q_out,

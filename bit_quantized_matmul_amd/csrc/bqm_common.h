@@ -112,10 +112,11 @@ hipError_t launch_cq_gemv_f32(const uint8_t *blob, const bqm_cq_layout &L, const
                               const float *x, int batch, float *y, int8_t *q_out,
                               float *scale_out, int num_cus, hipStream_t s);
 bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch);
-// Base-3 packed ternary (bits code 6): one token, up to 128 groups a row.
+// Base-3 packed ternary (bits code 6): one token with up to 128 groups a row,
+// or 2..16 tokens (launches of up to 4) with up to 64.
 bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch);
 hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
-                             const int8_t *q, const float *scale, float *y, int num_cus,
+                             const int8_t *q, const float *scale, int batch, float *y, int num_cus,
                              hipStream_t s);
 hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const int8_t *q, const float *scale, int batch, float *y,

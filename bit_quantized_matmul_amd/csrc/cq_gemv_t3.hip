@@ -1,4 +1,5 @@
-// Decode GEMV on base-3 packed ternary CQ weights (bits code 6), one token.
+// Decode GEMV on base-3 packed ternary CQ weights (bits code 6), 1..4 tokens a
+// launch (several tokens: rows of at most 64 groups).
 //
 // Format: the ternary CQ set of the Needle .cact/W4A8 article (section 1;
 // levels {-c, 0, +c}), with the indices packed five to a byte as base-3
@@ -7,7 +8,7 @@
 // (the zero level) past the group's end.
 //
 // The rotated-domain identity (article, section 3) gives
-//   y[n] = s * c / 128 * sum_g norm[n, g] * sum_{k in g} (idx[n, k] - 1) * q[k]
+//   y[b, n] = s_b * c / 128 * sum_g norm[n, g] * sum_{k in g} (idx[n, k] - 1) * q[b, k]
 // and the inner sum is an exact integer (|.| <= 128 * 127), so it runs on
 // v_dot4_i32_i8 with the digits as int8 -1 / 0 / +1.
 //
@@ -15,8 +16,9 @@
 //  * A lane owns SL (1 or 2) group slots, groups li and li + P, for every row
 //    it visits; a row takes P lanes (P a power of two, P * SL >= groups) and
 //    a wave holds 64 / P rows at a time.  The lane's activations never change,
-//    so they sit in registers, rearranged once (read from a copy of the
-//    token's codes that the workgroup stages in LDS, 144 bytes a group so that
+//    so they sit in registers for every token, rearranged once (read from a
+//    copy of the tokens' codes that the workgroup stages in LDS, 144 bytes a
+//    group so that
 //    16 lanes reading 16 groups hit distinct banks): for weight byte j, the int8
 //    codes at positions 5j .. 5j+3 as one dword, and the code at 5j+4 in
 //    byte j % 4 of dword j / 4 of a second set (7 dwords a group).
@@ -41,7 +43,8 @@ constexpr int kT3Copies = 16;                      // table copies
 constexpr int kT3Entries = 256;                    // every byte value (243.. are not digits: zeros)
 constexpr int kT3TableBytes = kT3Entries * kT3Copies * 8;   // 32 KB
 constexpr uint32_t kT3OOB = 0x80000000u;
-constexpr int kT3MaxGroups = 128;                  // cols <= 16384
+constexpr int kT3MaxGroups = 128;                  // cols <= 16384 (one token)
+constexpr int kT3MaxGroupsBatched = 64;            // cols <= 8192 (several tokens)
 constexpr int kT3QStride = kGroup + 16;            // bytes a group in the LDS copy of the codes
 typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
 
@@ -56,13 +59,13 @@ struct T3Load {
   uint32_t nw;
 };
 
-template <int SL>
+template <int SL, int BATCH>
 __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     const uint8_t *__restrict__ idx, uint32_t blob_bytes, const uint16_t *__restrict__ norms,
     uint32_t norm_bytes, const int8_t *__restrict__ q, const float *__restrict__ scale,
     float *__restrict__ y, int rows, int ng, int plog2, int passes_per_wave, float cfac) {
   __shared__ __align__(16) uint8_t tab[kT3TableBytes];
-  __shared__ __align__(16) uint8_t qlds[kT3MaxGroups * kT3QStride];
+  extern __shared__ __align__(16) uint8_t qlds[];   // [BATCH][ng][kT3QStride]
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int P = 1 << plog2;
@@ -91,9 +94,9 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     for (int c = 0; c < kT3Copies / 4; ++c) row[c] = make_uint4(lo, hi, lo, hi);
   }
 
-  // the token's codes into LDS, 16 bytes a thread per step
-  for (int c = t; c < ng * (kGroup / 16); c += kT3Threads) {
-    const int g = c >> 3, w = c & 7;
+  // the tokens' codes into LDS, 16 bytes a thread per step
+  for (int c = t; c < BATCH * ng * (kGroup / 16); c += kT3Threads) {
+    const int g = c >> 3, w = c & 7;               // g: token * ng + group (q is [BATCH][cols])
     *reinterpret_cast<u32x4t *>(qlds + g * kT3QStride + 16 * w) =
         *reinterpret_cast<const u32x4t *>(q + (size_t)c * 16);
   }
@@ -101,13 +104,15 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
 
   // the lane's activations per slot, five positions per weight byte
   constexpr int kQB = (kTritBytes + 3) / 4;
-  uint32_t qa[SL][kTritBytes], qb[SL][kQB];
+  uint32_t qa[SL][BATCH][kTritBytes], qb[SL][BATCH][kQB];
 #pragma unroll
-  for (int s = 0; s < SL; ++s) {
+  for (int s = 0; s < SL; ++s)
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
     const int g = li + P * s;
     uint32_t qw[kGroup / 4 + 1];
     if (g < ng) {
-      const u32x4t *src = reinterpret_cast<const u32x4t *>(qlds + g * kT3QStride);
+      const u32x4t *src = reinterpret_cast<const u32x4t *>(qlds + (b * ng + g) * kT3QStride);
 #pragma unroll
       for (int i = 0; i < kGroup / 16; ++i) {
         const u32x4t v = src[i];
@@ -119,13 +124,13 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
     }
     qw[kGroup / 4] = 0u;                           // positions 128.. read as 0 (their digits are 1)
 #pragma unroll
-    for (int i = 0; i < kQB; ++i) qb[s][i] = 0u;
+    for (int i = 0; i < kQB; ++i) qb[s][b][i] = 0u;
 #pragma unroll
     for (int j = 0; j < kTritBytes; ++j) {
       const int p = kTritsPerByte * j;             // positions p .. p + 4
-      qa[s][j] = __builtin_amdgcn_alignbyte(qw[(p >> 2) + 1], qw[p >> 2], p & 3);
+      qa[s][b][j] = __builtin_amdgcn_alignbyte(qw[(p >> 2) + 1], qw[p >> 2], p & 3);
       const int p4 = p + 4;
-      qb[s][j >> 2] |= ((qw[p4 >> 2] >> (8 * (p4 & 3))) & 0xFFu) << (8 * (j & 3));
+      qb[s][b][j >> 2] |= ((qw[p4 >> 2] >> (8 * (p4 & 3))) & 0xFFu) << (8 * (j & 3));
     }
   }
 
@@ -136,7 +141,9 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
   const uint32_t copyoff = (uint32_t)(lane & (kT3Copies - 1)) * 8u;
   const int wave_g = (int)((blockIdx.x * kT3Threads + t) >> 6);
   const int pass0 = wave_g * passes_per_wave;
-  const float sfac = scale[0] * cfac;
+  float sfac[BATCH];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) sfac[b] = scale[b] * cfac;
 
   // byte offset of slot s of row n (or past every range)
   auto woff = [&](int n, int s) -> uint32_t {
@@ -164,7 +171,9 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
   };
   auto compute = [&](T3Load (&L)[SL], int pass) {
     const int n = row_of(pass);
-    float part = 0.0f;
+    float part[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) part[b] = 0.0f;
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const uint32_t o = woff(n, s);
@@ -172,22 +181,34 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
       uint32_t r[7];
 #pragma unroll
       for (int i = 0; i < 7; ++i) r[i] = __builtin_amdgcn_alignbyte(L[s].w[i + 1], L[s].w[i], sh);
-      int acc = 0;
+      int acc[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) acc[b] = 0;
 #pragma unroll
       for (int j = 0; j < kTritBytes; ++j) {
         const uint32_t addr = ((r[j >> 2] >> (8 * (j & 3))) & 0xFFu) * (kT3Copies * 8u) + copyoff;
         const uint2 e = *reinterpret_cast<const uint2 *>(tab + addr);
-        acc = __builtin_amdgcn_sdot4((int)e.x, (int)qa[s][j], acc, false);
         // the fifth digit moves to byte j % 4, where its code sits
-        acc = __builtin_amdgcn_sdot4((int)(e.y << (8 * (j & 3))), (int)qb[s][j >> 2], acc, false);
+        const uint32_t e5 = e.y << (8 * (j & 3));
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          acc[b] = __builtin_amdgcn_sdot4((int)e.x, (int)qa[s][b][j], acc[b], false);
+          acc[b] = __builtin_amdgcn_sdot4((int)e5, (int)qb[s][b][j >> 2], acc[b], false);
+        }
       }
       const uint32_t no = noff(n, s);
       const float nrm = half_bits_to_float((uint16_t)(L[s].nw >> ((no & 2u) * 8u)));
-      part += (float)acc * nrm;                    // 0 for slots past the row (acc = 0)
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) part[b] += (float)acc[b] * nrm;   // 0 past the row (acc = 0)
     }
     // the row's P lanes add their parts (xor steps stay inside the segment)
-    for (int m = P >> 1; m > 0; m >>= 1) part += __shfl_xor(part, m, 64);
-    if (li == 0 && n < rows && pass < pass0 + passes_per_wave) y[n] = part * sfac;
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      for (int m = P >> 1; m > 0; m >>= 1) part[b] += __shfl_xor(part[b], m, 64);
+    if (li == 0 && n < rows && pass < pass0 + passes_per_wave) {
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) y[(size_t)b * rows + n] = part[b] * sfac[b];
+    }
   };
 
   T3Load A[SL], Bq[SL];
@@ -210,38 +231,62 @@ __global__ __launch_bounds__(kT3Threads) void cq_gemv_t3_kernel(
 
 bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch) {
   const int ng = L.cols / kGroup;
-  return batch == 1 && L.group == kGroup && L.cols % kGroup == 0 && ng >= 1 && ng <= 128 &&
-         L.total_bytes < ((int64_t)1 << 31);
+  const int max_groups = batch == 1 ? kT3MaxGroups : kT3MaxGroupsBatched;
+  return batch >= 1 && batch <= 16 && L.group == kGroup && L.cols % kGroup == 0 && ng >= 1 &&
+         ng <= max_groups && L.total_bytes < ((int64_t)1 << 31);
 }
 
-hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
-                             const int8_t *q, const float *scale, float *y, int num_cus,
-                             hipStream_t s) {
+namespace {
+
+template <int SL, int BATCH>
+hipError_t launch_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T, const int8_t *q,
+                     const float *scale, float *y, int num_cus, hipStream_t s) {
   const int ng = L.cols / kGroup;
-  const int sl = ng > 64 ? 2 : 1;
-  const int need = (ng + sl - 1) / sl;             // lanes per row
+  const int need = (ng + SL - 1) / SL;             // lanes per row
   int plog2 = 0;
   while ((1 << plog2) < need) ++plog2;
   const int rpp = 64 >> plog2;
   const long passes = ((long)L.rows + rpp - 1) / rpp;
-  const long waves_max = (long)num_cus * 2 * (kT3Threads / kWave);
+  // resident workgroups a CU: two, one when several tokens' codes in
+  // registers leave room for only two waves a SIMD
+  const long waves_max = (long)num_cus * (BATCH > 1 ? 1 : 2) * (kT3Threads / kWave);
   // at least 2 passes a wave (its activation set-up is not repeated per row),
-  // as many waves as that gives up to two workgroups a CU
+  // as many waves as that gives up to the resident workgroups
   const long waves = (passes + 1) / 2 < waves_max ? (passes + 1) / 2 : waves_max;
   const int per_wave = (int)((passes + waves - 1) / waves);
   const long used = (passes + per_wave - 1) / per_wave;          // waves with work
   const int blocks = (int)((used + (kT3Threads / kWave) - 1) / (kT3Threads / kWave));
   const uint16_t *norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
-  const uint32_t ib = (uint32_t)L.total_bytes;
   const uint32_t nb = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);
-  const float cfac = T.cscale / (float)kGroup;
-  if (sl == 1)
-    cq_gemv_t3_kernel<1><<<blocks, kT3Threads, 0, s>>>(blob, ib, norms, nb, q, scale, y, L.rows, ng, plog2,
-                                                       per_wave, cfac);
-  else
-    cq_gemv_t3_kernel<2><<<blocks, kT3Threads, 0, s>>>(blob, ib, norms, nb, q, scale, y, L.rows, ng, plog2,
-                                                       per_wave, cfac);
+  const size_t lds = (size_t)BATCH * ng * kT3QStride;   // the tokens' codes (the table is static)
+  cq_gemv_t3_kernel<SL, BATCH><<<blocks, kT3Threads, lds, s>>>(blob, (uint32_t)L.total_bytes, norms, nb, q,
+                                                               scale, y, L.rows, ng, plog2, per_wave,
+                                                               T.cscale / (float)kGroup);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                             const int8_t *q, const float *scale, int batch, float *y, int num_cus,
+                             hipStream_t s) {
+  if (batch == 1)
+    return L.cols / kGroup > 64 ? launch_t3<2, 1>(blob, L, T, q, scale, y, num_cus, s)
+                                : launch_t3<1, 1>(blob, L, T, q, scale, y, num_cus, s);
+  // several tokens (rows of at most 64 groups): launches of 4, 2 and 1 tokens,
+  // each one pass over the weights
+  for (int b0 = 0; b0 < batch;) {
+    const int nb = batch - b0 >= 4 ? 4 : (batch - b0 >= 2 ? 2 : 1);
+    const int8_t *qb = q + (size_t)b0 * L.cols;
+    float *yb = y + (size_t)b0 * L.rows;
+    hipError_t e;
+    if (nb == 4) e = launch_t3<1, 4>(blob, L, T, qb, scale + b0, yb, num_cus, s);
+    else if (nb == 2) e = launch_t3<1, 2>(blob, L, T, qb, scale + b0, yb, num_cus, s);
+    else e = launch_t3<1, 1>(blob, L, T, qb, scale + b0, yb, num_cus, s);
+    if (e != hipSuccess) return e;
+    b0 += nb;
+  }
+  return hipSuccess;
 }
 
 }  // namespace bqm

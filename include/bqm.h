@@ -116,9 +116,10 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * GEMV; for cols > 16384 batch > 4 runs on the cq_gemm kernel with that
  * kernel's arithmetic (level x norm/4 rounded to fp16 once per weight) and
  * smaller batches on the VALU GEMV, 4 tokens per launch.
- * Base-3 ternary (bits 6): batch 1 and cols <= 16384 only (BQM_ENOTSUP
- * otherwise); the group sums of digit x code are exact int32 dot products,
- * scaled by the fp32 norm and summed in fp32. */
+ * Base-3 ternary (bits 6): batch 1 with cols <= 16384, or 2 <= batch <= 16
+ * with cols <= 8192 (BQM_ENOTSUP otherwise), on the VALU path in launches of
+ * up to 4 tokens; the group sums of digit x code are exact int32 dot
+ * products, scaled by the fp32 norm and summed in fp32. */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
@@ -133,9 +134,10 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * quantizes the activations itself while its first weight loads are in
  * flight, with the VALU GEMV's arithmetic.  y equals act_fwht_quant_a8 then
  * cq_gemv bit for bit for batch 1, and whenever q_out and scale_out are
- * given.  The library allocates nothing.  Base-3 ternary (bits 6): batch 1,
- * and q_out (16-byte aligned) and scale_out are required (BQM_ENOTSUP
- * without them): act_fwht_quant_a8 into them, then the cq_gemv product. */
+ * given.  The library allocates nothing.  Base-3 ternary (bits 6): the
+ * cq_gemv limits, and q_out (16-byte aligned) and scale_out are required
+ * (BQM_ENOTSUP without them): act_fwht_quant_a8 into them, then the cq_gemv
+ * product. */
 int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);

@@ -451,6 +451,28 @@ def test_full_size_bit_sweep_sampled(code, codebooks):
         assert omm.rel_l2(y[:, sel], ref) <= TOL, (code, batch)
 
 
+# several tokens (rows of up to 64 groups): launches of 4, 2 and 1 tokens
+@pytest.mark.parametrize("rows,cols,batch", [(300, 512, 2), (130, 4096, 4), (77, 8192, 3), (33, 1024, 16),
+                                             (9, 640, 5), (1000, 384, 7)])
+def test_cq_gemv_ternary_b3_batched(rows, cols, batch, codebooks):
+    rng = np.random.default_rng(490 + rows + cols + batch)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, ocq.TERNARY_B3, batch, codebooks)
+    ref = omm.cq_reference(idx, n16, 128, ocq.TERNARY_B3, lv, q, s)
+    lay = B.cq_pack_info(rows, cols, 128, ocq.TERNARY_B3)
+    y = host(B.cq_gemv(dev(blob), lay, None, dev(q), dev(s)))
+    assert omm.rel_l2(y, ref) <= TOL
+    # each token equals the one-token product on its own, bit for bit
+    for b in (0, batch - 1):
+        y1 = host(B.cq_gemv(dev(blob), lay, None, dev(q[b:b + 1]), dev(s[b:b + 1])))
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+    x = inputs.activations(rng, batch, cols)
+    q_out = torch.empty((batch, cols), dtype=torch.int8, device=DEV)
+    s_out = torch.empty((batch,), dtype=torch.float32, device=DEV)
+    yf = host(B.cq_gemv_f32(dev(blob), lay, None, dev(x), q_out=q_out, scale_out=s_out))
+    y2 = host(B.cq_gemv(dev(blob), lay, None, q_out, s_out))
+    assert np.array_equal(yf.view(np.uint32), y2.view(np.uint32))
+
+
 @pytest.mark.parametrize("rows,cols", [(14336, 4096), (4096, 14336)])
 def test_full_size_ternary_b3_sampled(rows, cols):
     """Base-3 ternary at the sweep and down-projection shapes, one token, in
