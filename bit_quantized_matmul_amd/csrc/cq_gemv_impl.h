@@ -39,7 +39,7 @@ namespace {
 // current and next row of index words in registers.
 template <int CPL> constexpr int block_threads() { return CPL >= 4 ? 512 : 1024; }
 constexpr size_t kMaxActLds = 72 * 1024;   // LDS for the fp16 activations (table: 64 KB)
-constexpr int kMaxFusedCols = 16384;       // fused A8: a thread holds <= 2 segments of 32
+constexpr int kMaxFusedCols = 16384;       // fused A8: the widest row (registers hold its 16-element segments)
 constexpr int kRingChunks = 8;             // 32-index chunks a lane keeps in flight
 constexpr int kMaxRowsBlk = 512;           // rows x K-split waves a workgroup finishes
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
