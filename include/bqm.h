@@ -15,8 +15,8 @@
  *   - Every argument is validated on the host before anything is launched.
  *     The return value is BQM_OK (0) or a negative BQM_E* code; after a
  *     validation error nothing has been enqueued.  BQM_EDEVICE reports a HIP
- *     error seen while launching (hipGetLastError); a call made of two
- *     launches may then have enqueued the first.
+ *     error seen while launching (hipGetLastError); a call made of several
+ *     launches may then have enqueued the ones before the failing launch.
  *   - Matrices are row-major.  Weight matrices are [out, in] = [rows, cols]:
  *     every output row is contiguous along the reduction axis and quant
  *     groups run along that axis ("14MB holds 45M parameters: dissecting
