@@ -10,6 +10,12 @@ scale the device consumed (this isolates the matmul from A8 rounding).
 ``cq_rotated`` is the rotated-domain form the device uses,
 y = s_b / G * sum_g norm[n, g] * dot(cb[idx[n, g]], q[b, g]); the two agree
 in real arithmetic because H_u H_u = G I (checked by the tests to 1e-12).
+
+``cq_magnitude`` and ``q4_0_magnitude`` are the sums of the absolute values
+of the terms of those sums (the rotated-domain terms for CQ).  Rounding a
+sum of terms in floating point, whatever the order, errs by at most a small
+multiple of the unit roundoff times this magnitude, so it is the scale that
+per-element tolerances are stated against.
 """
 from __future__ import annotations
 
@@ -39,10 +45,28 @@ def cq_rotated(idx, norm16, group, code, levels, q, s) -> np.ndarray:
     return y * (np.asarray(s, dtype=np.float64)[:, None] / group)
 
 
+def cq_magnitude(idx, norm16, group, code, levels, q, s) -> np.ndarray:
+    """s_b/G * sum_g norm[n, g] * sum_{i in g} |cb[idx[n, i]]| * |q[b, i]|, fp64."""
+    rows, cols = idx.shape
+    ng = cols // group
+    c = np.abs(_cq.level_values(idx, code, levels)).reshape(rows, ng, group)
+    n = np.abs(np.asarray(norm16, dtype=np.float16).astype(np.float64))
+    qq = np.abs(np.asarray(q, dtype=np.float64)).reshape(q.shape[0], ng, group)
+    acc = np.einsum("ngi,bgi->bng", c, qq)
+    y = np.einsum("bng,ng->bn", acc, n)
+    return y * (np.abs(np.asarray(s, dtype=np.float64))[:, None] / group)
+
+
 def q4_0_reference(blocks, cols, x) -> np.ndarray:
     """y[b, r] = sum_{k < cols} W_hat[r, k] * x[b, k] in fp64."""
     w_hat = _q4.decode(blocks, cols)
     return np.asarray(x, dtype=np.float64) @ w_hat.T
+
+
+def q4_0_magnitude(blocks, cols, x) -> np.ndarray:
+    """sum_{k < cols} |W_hat[r, k]| * |x[b, k]| in fp64."""
+    w_hat = _q4.decode(blocks, cols)
+    return np.abs(np.asarray(x, dtype=np.float64)) @ np.abs(w_hat).T
 
 
 def rel_l2(y, ref) -> float:

@@ -57,6 +57,40 @@ def test_a8_dequant_inverts_rotation():
     assert np.allclose(a8.dequant_a8(q, ss, g), x, atol=1e-12)
 
 
+def _sparse(spec: str, n: int = 128) -> np.ndarray:
+    v = np.zeros(n, dtype=np.float64)
+    for item in spec.split():
+        i, val = item.split(":")
+        v[int(i)] = float(val)
+    return v
+
+
+def tie_rows():
+    """Rows of tests/golden/a8_ties.txt as (x fp32 [128], s, q [128]).
+
+    x = H_u u / 128 with H_u from the bit-parity closed form; every value is
+    exact in fp32, so H_u x = u exactly (H_u H_u = 128 I)."""
+    g = {r[0].split(":", 1)[0]: r[0].split(":", 1)[1].strip() for r in read_golden_rows("a8_ties.txt")}
+    hu = parity_hadamard(128).astype(np.float64)
+    out = []
+    for r in range(2):
+        u = _sparse(g[f"row{r}_u"])
+        x64 = (hu @ u) / 128.0
+        x32 = x64.astype(np.float32)
+        assert np.array_equal(x32.astype(np.float64), x64)
+        out.append((x32, float(g[f"row{r}_s"]), _sparse(g[f"row{r}_q"]).astype(np.int64)))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["fp32", "fp64"])
+def test_a8_ties_round_half_to_even(mode):
+    """Hand-worked codes for exact .5 quotients (half-even; half-away would differ)."""
+    for x, s_want, q_want in tie_rows():
+        q, s = a8.act_quant_a8(x[None, :], 128, mode)
+        assert float(s[0]) == s_want
+        assert np.array_equal(q[0].astype(np.int64), q_want)
+
+
 # --------------------------------------------------------------------- Q4_0
 
 def test_q4_0_hand_built_block():
@@ -204,3 +238,45 @@ def test_q4_0_reference_brute_force():
 def test_rel_l2():
     assert matmul.rel_l2([1.0, 2.0], [1.0, 2.0]) == 0.0
     assert math.isclose(matmul.rel_l2([1.0, 0.0], [0.0, 0.0]), 1.0)
+
+
+@pytest.mark.parametrize("code", [1, 4, 5])
+def test_cq_magnitude_bounds_and_equality(code, codebooks):
+    """The magnitude is >= |y| for every element (triangle inequality) and equals
+    the product itself when every term is non-negative (non-negative codes and
+    only non-negative levels), where the plain definition is pinned by brute force."""
+    rng = np.random.default_rng(60 + code)
+    w = (0.02 * rng.standard_normal((20, 256))).astype(np.float32)
+    w[3] *= 1e-4
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    lv = cq.levels_for(code, codebooks)
+    idx, n16 = cq.encode(w, 128, code, lv)
+    q, s = a8.act_quant_a8(x, 128, "fp32")
+    y = matmul.cq_reference(idx, n16, 128, code, lv, q, s)
+    mag = matmul.cq_magnitude(idx, n16, 128, code, lv, q, s)
+    assert np.all(np.abs(y) <= mag * (1 + 1e-12))
+    assert np.all(mag > 0)
+    # every index at the largest (positive) level, codes |q|: all terms >= 0
+    top = np.full_like(idx, int(np.argmax(lv)))
+    qa = np.abs(q.astype(np.int64)).astype(np.int8)
+    yp = matmul.cq_reference(top, n16, 128, code, lv, qa, s)
+    mp = matmul.cq_magnitude(top, n16, 128, code, lv, qa, s)
+    assert np.allclose(mp, yp, rtol=1e-12, atol=0)
+    # signs do not matter to the magnitude
+    qf = qa.copy()
+    qf[:, ::3] = -qf[:, ::3]
+    assert np.array_equal(matmul.cq_magnitude(top, n16, 128, code, lv, qf, s), mp)
+
+
+def test_q4_0_magnitude_bounds_and_equality():
+    rng = np.random.default_rng(61)
+    w = (0.02 * rng.standard_normal((7, 70))).astype(np.float32)
+    x = rng.standard_normal((2, 70)).astype(np.float32)
+    blk = q4_0.encode(w)
+    y = matmul.q4_0_reference(blk, 70, x)
+    mag = matmul.q4_0_magnitude(blk, 70, x)
+    assert np.all(np.abs(y) <= mag * (1 + 1e-12)) and np.all(mag > 0)
+    wp = np.abs(w)
+    blp = q4_0.encode(wp)
+    xp = np.abs(x)
+    assert np.allclose(matmul.q4_0_magnitude(blp, 70, xp), matmul.q4_0_reference(blp, 70, xp), rtol=1e-12)
