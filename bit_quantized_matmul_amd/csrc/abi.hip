@@ -95,6 +95,22 @@ bool is_bf16_exact(float f) { return (__builtin_bit_cast(uint32_t, f) & 0xFFFFu)
 
 bool f16_exact(float f) { return (float)(_Float16)f == f; }
 
+// 13 - max(floor(log2(max |level|)), -1) over the fp16 levels of the table
+// (0 for an all-zero table): the GEMM scales a row's norms by 2^(this - E_M),
+// E_M = floor(log2(the row's largest norm)), which keeps level x norm x scale
+// and norm x scale below 2^15.
+int fold_exp_of(const LevelTable &T) {
+  float mx = 0.0f;
+  for (int l = 0; l < T.levels; ++l) mx = fmaxf(mx, fabsf((float)__builtin_bit_cast(_Float16, T.h16[l])));
+  int e = -1;
+  if (mx > 0.0f) {
+    int ex;
+    frexpf(mx, &ex);                               // mx = f * 2^ex, f in [0.5, 1)
+    e = ex - 1 > -1 ? ex - 1 : -1;
+  }
+  return 13 - e;
+}
+
 // Build the kernels' level table.  Fitted codebooks must be finite and
 // bfloat16-representable (then they are exact in fp16 and bf16 alike).
 int make_table(int bits, const float *codebook, LevelTable *T) {
@@ -115,6 +131,7 @@ int make_table(int bits, const float *codebook, LevelTable *T) {
       T->f32[l] = sg[l] * cf;
     }
     T->cscale = cf;
+    T->fold_exp = fold_exp_of(*T);
     return BQM_OK;
   }
   if (codebook == nullptr) return BQM_EINVAL;
@@ -126,6 +143,7 @@ int make_table(int bits, const float *codebook, LevelTable *T) {
     T->f32[l] = v;
   }
   T->cscale = 1.0f;
+  T->fold_exp = fold_exp_of(*T);
   return BQM_OK;
 }
 
@@ -273,7 +291,9 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
 int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
               bqm_stream_t stream) {
   if (!blocks || !x || !y || rows < 1 || cols < 1 || batch < 1) return BQM_EINVAL;
-  if (batch > 16) return BQM_ENOTSUP;
+  // the kernel addresses the blocks with 32-bit offsets
+  if (batch > 16 || (int64_t)rows * (((int64_t)cols + 31) / 32) * 18 >= ((int64_t)1 << 31))
+    return BQM_ENOTSUP;
   if (!aligned16(blocks) || !aligned16(x) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
   int cus;
   const int rc = current_device(&cus);

@@ -24,6 +24,7 @@ struct LevelTable {
   uint16_t b16[16];
   float f32[16];    // fp32 levels (cb or c*sign), used by the encoder
   float cscale;
+  int fold_exp;     // 13 - max(floor(log2(max |h16 level|)), -1): the GEMM's row exponent base
   int bits;         // bits code 1..6
   int index_bits;   // 1..4; 0 for base-3 ternary (five indices a byte)
   int levels;       // 2, 4, 8, 16 or 3

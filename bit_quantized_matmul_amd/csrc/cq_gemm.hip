@@ -15,12 +15,19 @@
 //  * B (weights): each wave looks its own fragment up straight into registers
 //    from an LDS table indexed by an index byte (the same replicated,
 //    bank-conflict-free table as the GEMV), and scales each fp16 level pair by
-//    the group's norm / 4 with one packed fp16 multiply.  That product is the
-//    one rounding of the path (<= 2^-11 relative per weight, ~3e-4 on y); the
-//    1/4 keeps level x norm (levels <= 2.74) inside the fp16 range for any
-//    fp16 norm.  MFMA products of fp16 operands are exact and accumulate in
-//    fp32 (v_mfma_f32_32x32x16_f16) straight through all of K: no per-group
-//    epilogue interrupts the chain.
+//    the group's norm times 2^e_n with one packed fp16 multiply.  e_n is an
+//    exponent per weight row n, chosen from the row's largest norm so that
+//    level x norm x 2^e_n stays below 2^15 for every level and group of the
+//    row; norm x 2^e_n is formed exactly in fp32 and converted exactly to
+//    fp16.  The packed multiply is then the one rounding of the path: at most
+//    2^-11 relative per weight for every group whose products stay in fp16's
+//    normal range, i.e. whose norm is at least ~2^-23 of the row's largest
+//    (smaller groups round to fp16 subnormals, an absolute error below
+//    2^-39 of the row's largest level x norm per weight).  MFMA products of
+//    fp16 operands are exact and accumulate in fp32
+//    (v_mfma_f32_32x32x16_f16) straight through all of K: no per-group
+//    epilogue interrupts the chain.  The epilogue multiplies each column by
+//    2^-e_n, exactly.
 //  * The k order inside a group is permuted consistently for A and B: in step
 //    s (0..7) lane half h supplies columns 64h + 8s .. +8, so each lane reads
 //    one contiguous run of 64 indices per group.
@@ -240,6 +247,49 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     bbase[nb] = ok ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh + 4 * IB * kh) : kOOB;
     nbase[nb] = ok ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
   }
+  // The row exponents: each lane needs e_n for its NB rows.  The two lanes of
+  // a wave that supply row n (lane halves lh = 0, 1) read alternate pieces of
+  // the row's norms (16-byte pieces of 8 norms when the group count is a
+  // multiple of 8, else single norms) and combine their maxima.  Norms are
+  // non-negative, so their fp16 bit patterns order as their values.  The
+  // first batch of loads (up to 64 groups a row) is issued here, before the
+  // main loads, and reduced after them; longer rows finish in a loop.
+  constexpr int kPre = 4;                          // pre-pass loads per row and batch
+  constexpr int kPerLoad = N8 ? 8 : 1;             // norms per pre-pass load
+  const int pieces = N8 ? ng / 8 : ng;
+  uint32_t pre[kPre][NB][N8 ? 4 : 1];
+  auto issue_pre = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int j = j0 + 2 * u;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t off = j < pieces ? nbase[nb] + (uint32_t)(2 * kPerLoad * j) : kOOB;
+        if constexpr (N8) {
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, off, 0, 0));
+          pre[u][nb][0] = v.x; pre[u][nb][1] = v.y; pre[u][nb][2] = v.z; pre[u][nb][3] = v.w;
+        } else {
+          pre[u][nb][0] = __builtin_amdgcn_raw_buffer_load_b16(rn, off, 0, 0);
+        }
+      }
+    }
+  };
+  uint32_t nmax[NB];
+  auto reduce_pre = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < (N8 ? 4 : 1); ++i) {
+          const uint32_t w = pre[u][nb][i];
+          nmax[nb] = max(nmax[nb], max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+        }
+  };
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) nmax[nb] = 0;
+  issue_pre(lh);
+
   // Each n-block walks the groups from its own starting point (wrapping), so
   // the n-blocks that share A rows read different k-slices at any one time
   // instead of all hitting the same memory channels together.  The m-tiles of
@@ -296,6 +346,29 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   if constexpr (N8) issue_norms(0, ncur);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(d, d);
+  // the rest of the row exponents' pre-pass (the first batch has landed by
+  // the time the first A stores wait for their loads)
+  reduce_pre();
+  for (int j0 = 2 * kPre; j0 < pieces; j0 += 2 * kPre) {   // a trip count the wave shares
+    issue_pre(j0 + lh);
+    reduce_pre();
+  }
+  // e_n = fold_exp - E_M with E_M = floor(log2(largest norm)): then
+  // norm x 2^e_n < 2^15 and level x norm x 2^e_n < 2^15 for every level
+  // (fold_exp = 13 - max(floor(log2(largest |level|)), -1), from the host)
+  float rsc[NB], rinv[NB];                         // 2^e_n and 2^-e_n
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t hm = max(nmax[nb], (uint32_t)__shfl_xor((int)nmax[nb], 32, 64));
+    int e;
+    if (hm == 0) e = 0;                            // an all-zero row (or a row past N)
+    else if (hm >= 0x7C00u) e = -2;                // inf / NaN norms: no scaling can help
+    else if (hm >= 0x400u) e = T.fold_exp - ((int)(hm >> 10) - 15);
+    else e = T.fold_exp - ((31 - __builtin_clz(hm)) - 24);   // subnormal largest norm
+    rsc[nb] = __uint_as_float((uint32_t)(127 + e) << 23);
+    rinv[nb] = __uint_as_float((uint32_t)(127 - e) << 23);
+  }
+
 #pragma unroll
   for (int i = 0; i < kAV; ++i) store_a_part(0, 0, i);
   __syncthreads();
@@ -323,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     }
     return o;
   };
-  // group g's norm / 4 as an fp16 pair (scaling by 1/4 is exact): from
+  // group g's norm x 2^e_n as an fp16 pair (formed exactly in fp32): from
   // prefetch slot d, or (N8) from this loop round's or the next one's norms,
   // where group g is halfword g % 8
   auto take_group = [&](int g, int d, bool next) {
@@ -337,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
       } else {
         nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
       }
-      const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)nw) * (_Float16)(g < ng ? 0.25f : 0.0f);
+      const _Float16 h = (_Float16)(half_bits_to_float((uint16_t)nw) * (g < ng ? rsc[nb] : 0.0f));
       nq[nb] = h2v{h, h};
     }
   };
@@ -404,13 +477,14 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     return (32 * MB * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3)) * kYS + 32 * NB * wn + 32 * nb + lr;
   };
   __syncthreads();                                 // every wave is done with the table and A buffers
+  // (column lr of tile nb is weight row ncol[nb]: its 2^-e_n is exact)
   if (kh == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ys[ypos(mb, nb, r)] = acc[mb][nb][r];
+        for (int r = 0; r < 16; ++r) ys[ypos(mb, nb, r)] = acc[mb][nb][r] * rinv[nb];
   }
   __syncthreads();
   if (kh == 0) {
@@ -421,11 +495,11 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int p = ypos(mb, nb, r);
-          ys[p] = acc[mb][nb][r] + ys[p];
+          ys[p] = acc[mb][nb][r] * rinv[nb] + ys[p];
         }
   }
   __syncthreads();
-  const float cfac = T.cscale * (4.0f / kGroup);     // the B operand carries norm / 4
+  const float cfac = T.cscale * (1.0f / kGroup);
   constexpr int kLPR = kBN / 4;                    // threads per tile row, 4 columns each
   constexpr int kRPP = kThreads / kLPR;            // rows per pass
   const int cr = t / kLPR, cc = (t % kLPR) * 4;

@@ -20,6 +20,11 @@ Workload recipes (weights are 0.02*N(0,1), activations N(0,1)):
   4096x4096 without outliers.
 * ``cq_bit_sweep``: one 14336x4096 matrix with 1% outlier rows, activations
   for batch 1, 4 and 16.
+* ``weight_matrix_mixed`` (parity tests): 0.02*N(0,1) rows among which every
+  7th row is scaled by 1e-3, every 11th by 1e-4, every 13th by 1e-6, one row
+  has its groups alternately scaled by 1 and 1e-4, and one row is all zero,
+  so that group norms span fp16 from its normal range deep into its
+  subnormals within one matrix.
 """
 from __future__ import annotations
 
@@ -69,6 +74,26 @@ def weight_matrix(rng: np.random.Generator, rows: int, cols: int,
         n_out = int(math.ceil(OUTLIER_FRACTION * rows))
         sel = rng.choice(rows, n_out, replace=False)
         w[sel] *= np.float32(OUTLIER_SCALE)
+    return w
+
+
+MIXED_ROW_SCALES = ((7, 1e-3), (11, 1e-4), (13, 1e-6))
+
+
+def weight_matrix_mixed(rng: np.random.Generator, rows: int, cols: int, group: int = 128,
+                        outliers: bool = False) -> np.ndarray:
+    """``weight_matrix`` with rows at very different scales (see the module notes):
+    rows r with r % p == p - 1 scaled by f for each (p, f) of MIXED_ROW_SCALES
+    (later entries win), row 1 with its odd groups scaled by 1e-4 (when there is
+    more than one group) and row rows // 2 set to zero."""
+    w = weight_matrix(rng, rows, cols, outliers=outliers)
+    r = np.arange(rows)
+    for period, f in MIXED_ROW_SCALES:
+        w[r % period == period - 1] *= np.float32(f)
+    if rows > 1 and cols > group:
+        g = w[1].reshape(-1, group)
+        g[1::2] *= np.float32(1e-4)
+    w[rows // 2] = 0.0
     return w
 
 

@@ -114,8 +114,11 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * exact fp16 codes, fp32 accumulation per group, fp32 norm per group, the
  * groups summed in a fixed order.  Batch 1 and 2 otherwise run on the VALU
  * GEMV; for cols > 16384 batch > 4 runs on the cq_gemm kernel with that
- * kernel's arithmetic (level x norm/4 rounded to fp16 once per weight) and
- * smaller batches on the VALU GEMV, 4 tokens per launch.
+ * kernel's arithmetic and bound (level x norm x 2^e_n rounded to fp16 once
+ * per weight, see cq_gemm) and smaller batches on the VALU GEMV, 4 tokens per
+ * launch.  The VALU and matrix-core routes form every product level x code
+ * exactly, so each y[b, n] is within a few units of fp32 roundoff of
+ * scale[b] / G * sum_g norm[n, g] * sum_i |cb[idx[n, i]]| * |q[b, i]|.
  * Base-3 ternary (bits 6): batch 1 with cols <= 16384, or 2 <= batch <= 16
  * with cols <= 8192 (BQM_ENOTSUP otherwise), on the VALU path in launches of
  * up to 4 tokens; the group sums of digit x code are exact int32 dot
@@ -146,9 +149,17 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
  * GEMM with the same layout, every row one reduction stream).  Same sum as
  * cq_gemv for m tokens: q [device] int8 [m, cols], scale [device] fp32 [m],
  * y [device] fp32 [m, rows].  The weight tile is the codebook level times
- * the group norm, rounded once to fp16 (relative error <= 2^-11 per weight);
- * activations enter as exact fp16 integers; the matrix cores accumulate in
- * fp32 and the token scale is applied in fp32.  m >= 1, group must be 128.
+ * the group norm times 2^e_n, rounded once to fp16, where e_n is a power of
+ * two per weight row chosen from the row's largest norm (level x norm x 2^e_n
+ * < 2^15) and undone exactly in the fp32 epilogue.  The rounding error is at
+ * most 2^-11 relative per weight for every group whose norm is at least
+ * 2^-23 of its row's largest (for smaller ones the product may round to an
+ * fp16 subnormal: an absolute error below 2^-39 of the row's largest
+ * level x norm per weight), so each y[m, n] is within 2^-11 (plus fp32
+ * roundoff) of scale[m] / G * sum_g norm[n, g] * sum_i |cb[idx[n, i]]| *
+ * |q[m, i]| of the exact sum, at any scale of the row.  Activations enter as
+ * exact fp16 integers; the matrix cores accumulate in fp32 and the token
+ * scale is applied in fp32.  m >= 1, group must be 128.
  * Returns BQM_ENOTSUP when the packed indices or m * cols exceed 2^30 bytes
  * (the kernel addresses them with 32-bit offsets), and for base-3 ternary
  * (bits 6), which has a decode product only. */
@@ -161,7 +172,9 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * nibble the even element; weight = (nibble - 8) * d; rows are zero-padded to
  * a multiple of 32 so a block never straddles two rows.
  * x [device] fp32 [batch, cols] (no padding needed: columns >= cols are never
- * read); y [device] fp32 [batch, rows].  1 <= batch <= 16. */
+ * read); y [device] fp32 [batch, rows].  1 <= batch <= 16.  Returns
+ * BQM_ENOTSUP when the blocks reach 2^31 bytes (rows * ceil(cols/32) * 18:
+ * the kernel addresses them with 32-bit offsets) or batch > 16. */
 int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
               bqm_stream_t stream);
 

@@ -74,3 +74,13 @@ def codebooks(raw_fits):
     """Shipped cb2/cb3/cb4 tables (bf16-rounded oracle fits)."""
     from oracle import codebook
     return {b: codebook.shipped_table(r) for b, r in raw_fits.items()}
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print the element-wise parity statistics the GPU tests recorded."""
+    try:
+        from tests import parity
+    except Exception:
+        return
+    for line in parity.summary_lines():
+        terminalreporter.write_line(line)
