@@ -135,12 +135,15 @@ def cq_analytic_levels(bits: int) -> np.ndarray:
     return np.array(out[:n], dtype=np.float32)
 
 
-def _codebook_ptr(codebook):
-    """Host fp32 array (or None) -> (ctypes pointer, keep-alive object)."""
+def _codebook_ptr(codebook, levels=None):
+    """Host fp32 array (or None) -> (ctypes pointer, keep-alive object).  The
+    library reads `levels` values from it, so a shorter array is rejected."""
     if codebook is None:
         return None, None
     arr = np.ascontiguousarray(np.asarray(codebook.cpu() if hasattr(codebook, "cpu") else codebook,
-                                          dtype=np.float32))
+                                          dtype=np.float32)).ravel()
+    if levels is not None and arr.size != levels:
+        raise ValueError(f"codebook must hold {levels} levels, got {arr.size}")
     return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), arr
 
 
@@ -154,6 +157,30 @@ def _torch():
 def _stream():
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _shape(t, shape, name):
+    """Check a tensor's shape before any pointer reaches the library (a wrong
+    shape would send device reads or writes past the tensor)."""
+    got = tuple(getattr(t, "shape", ()))
+    if got != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+
+
+def _at_least(t, nbytes, name):
+    """Check that a byte buffer holds at least `nbytes` elements."""
+    n = t.numel() if hasattr(t, "numel") else np.asarray(t).size
+    if n < nbytes:
+        raise ValueError(f"{name} must hold at least {nbytes} bytes, got {n}")
+
+
+def _rows2d(t, cols, name):
+    """A 2-D [batch, cols] tensor's batch."""
+    if getattr(t, "ndim", 0) != 2 or t.shape[1] != cols:
+        raise ValueError(f"{name} must have shape [batch, {cols}], got {tuple(getattr(t, 'shape', ()))}")
+    if t.shape[0] < 1:
+        raise ValueError(f"{name} must have at least one row")
+    return int(t.shape[0])
 
 
 def _dev(t, dtype, name):
@@ -170,11 +197,15 @@ def _dev(t, dtype, name):
 def act_fwht_quant_a8(x, group: int = GROUP, q=None, scale=None):
     """x fp32 [m, k] -> (q int8 [m, k], scale fp32 [m])."""
     torch = _torch()
+    if getattr(x, "ndim", 0) != 2:
+        raise ValueError(f"x must be 2-D [m, k], got {tuple(getattr(x, 'shape', ()))}")
     m, k = x.shape
     if q is None:
         q = torch.empty((m, k), dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _shape(q, (m, k), "q")
+    _shape(scale, (m,), "scale")
     _check("act_fwht_quant_a8", load_library().act_fwht_quant_a8(
         _dev(x, torch.float32, "x"), m, k, group, _dev(q, torch.int8, "q"),
         _dev(scale, torch.float32, "scale"), _stream()))
@@ -184,10 +215,13 @@ def act_fwht_quant_a8(x, group: int = GROUP, q=None, scale=None):
 def cq_gemv(blob, layout: CqLayout, codebook, q, scale, y=None):
     """Packed CQ [rows, cols] x int8 q [batch, cols] -> fp32 y [batch, rows]."""
     torch = _torch()
-    batch = q.shape[0]
+    batch = _rows2d(q, layout.cols, "q")
+    _at_least(blob, layout.total_bytes, "blob")
+    _shape(scale, (batch,), "scale")
     if y is None:
         y = torch.empty((batch, layout.rows), dtype=torch.float32, device=q.device)
-    cb, _keep = _codebook_ptr(codebook)
+    _shape(y, (batch, layout.rows), "y")
+    cb, _keep = _codebook_ptr(codebook, layout.levels)
     _check("cq_gemv", load_library().cq_gemv(
         _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
         _dev(scale, torch.float32, "scale"), batch, _dev(y, torch.float32, "y"), _stream()))
@@ -198,10 +232,16 @@ def cq_gemv_f32(blob, layout: CqLayout, codebook, x, y=None, q_out=None, scale_o
     """Packed CQ [rows, cols] x fp32 x [batch, cols] -> fp32 y [batch, rows]; the A8
     step runs inside the GEMV launch (optional q_out / scale_out receive the codes)."""
     torch = _torch()
-    batch = x.shape[0]
+    batch = _rows2d(x, layout.cols, "x")
+    _at_least(blob, layout.total_bytes, "blob")
     if y is None:
         y = torch.empty((batch, layout.rows), dtype=torch.float32, device=x.device)
-    cb, _keep = _codebook_ptr(codebook)
+    _shape(y, (batch, layout.rows), "y")
+    if q_out is not None:
+        _shape(q_out, (batch, layout.cols), "q_out")
+    if scale_out is not None:
+        _shape(scale_out, (batch,), "scale_out")
+    cb, _keep = _codebook_ptr(codebook, layout.levels)
     qo = _dev(q_out, torch.int8, "q_out") if q_out is not None else None
     so = _dev(scale_out, torch.float32, "scale_out") if scale_out is not None else None
     _check("cq_gemv_f32", load_library().cq_gemv_f32(
@@ -213,10 +253,13 @@ def cq_gemv_f32(blob, layout: CqLayout, codebook, x, y=None, q_out=None, scale_o
 def cq_gemm(blob, layout: CqLayout, codebook, q, scale, y=None):
     """Packed CQ [rows, cols] x int8 q [m, cols] -> fp32 y [m, rows] (matrix cores)."""
     torch = _torch()
-    m = q.shape[0]
+    m = _rows2d(q, layout.cols, "q")
+    _at_least(blob, layout.total_bytes, "blob")
+    _shape(scale, (m,), "scale")
     if y is None:
         y = torch.empty((m, layout.rows), dtype=torch.float32, device=q.device)
-    cb, _keep = _codebook_ptr(codebook)
+    _shape(y, (m, layout.rows), "y")
+    cb, _keep = _codebook_ptr(codebook, layout.levels)
     _check("cq_gemm", load_library().cq_gemm(
         _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
         _dev(scale, torch.float32, "scale"), m, _dev(y, torch.float32, "y"), _stream()))
@@ -226,9 +269,11 @@ def cq_gemm(blob, layout: CqLayout, codebook, q, scale, y=None):
 def q4_0_gemv(blocks, rows: int, cols: int, x, y=None):
     """Q4_0 blocks [rows, ceil(cols/32), 18] x fp32 x [batch, cols] -> fp32 y [batch, rows]."""
     torch = _torch()
-    batch = x.shape[0]
+    batch = _rows2d(x, cols, "x")
+    _at_least(blocks, q4_0_nbytes(rows, cols), "blocks")
     if y is None:
         y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
+    _shape(y, (batch, rows), "y")
     _check("q4_0_gemv", load_library().q4_0_gemv(
         _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), batch,
         _dev(y, torch.float32, "y"), _stream()))
@@ -238,9 +283,11 @@ def q4_0_gemv(blocks, rows: int, cols: int, x, y=None):
 def q4_0_gemm(blocks, rows: int, cols: int, x, y=None):
     """Q4_0 blocks [rows, ceil(cols/32), 18] x fp32 x [m, cols] -> fp32 y [m, rows]."""
     torch = _torch()
-    m = x.shape[0]
+    m = _rows2d(x, cols, "x")
+    _at_least(blocks, q4_0_nbytes(rows, cols), "blocks")
     if y is None:
         y = torch.empty((m, rows), dtype=torch.float32, device=x.device)
+    _shape(y, (m, rows), "y")
     _check("q4_0_gemm", load_library().q4_0_gemm(
         _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), m,
         _dev(y, torch.float32, "y"), _stream()))
@@ -293,6 +340,7 @@ def kmcu_upload(file, tensor: KmcuTensor, dst=None):
     torch = _torch()
     if dst is None:
         dst = torch.empty((tensor.nbytes,), dtype=torch.uint8, device="cuda")
+    _at_least(dst, tensor.nbytes, "dst")
     p, n, _keep = _host_bytes(file)
     _check("kmcu_upload", load_library().kmcu_upload(p, n, ctypes.byref(tensor),
                                                      _dev(dst, torch.uint8, "dst"), _stream()))
@@ -331,9 +379,13 @@ def kmcu_load(file):
 def cq_pack(w, layout: CqLayout, codebook, blob=None, status=None):
     """fp32 W [rows, cols] -> packed blob (uint8 [total_bytes]) on the device."""
     torch = _torch()
+    _shape(w, (layout.rows, layout.cols), "w")
     if blob is None:
         blob = torch.empty((layout.total_bytes,), dtype=torch.uint8, device=w.device)
-    cb, _keep = _codebook_ptr(codebook)
+    _at_least(blob, layout.total_bytes, "blob")
+    if status is not None and status.numel() < 1:
+        raise ValueError("status must hold one int32")
+    cb, _keep = _codebook_ptr(codebook, layout.levels)
     st = _dev(status, torch.int32, "status") if status is not None else None
     _check("cq_pack", load_library().cq_pack(
         _dev(w, torch.float32, "w"), ctypes.byref(layout), cb, _dev(blob, torch.uint8, "blob"),
@@ -348,9 +400,12 @@ def q4_0_nbytes(rows: int, cols: int) -> int:
 def q4_0_pack(w, blocks=None):
     """fp32 W [rows, cols] -> Q4_0 blocks (uint8 [rows*ceil(cols/32)*18])."""
     torch = _torch()
+    if getattr(w, "ndim", 0) != 2:
+        raise ValueError(f"w must be 2-D [rows, cols], got {tuple(getattr(w, 'shape', ()))}")
     rows, cols = w.shape
     if blocks is None:
         blocks = torch.empty((q4_0_nbytes(rows, cols),), dtype=torch.uint8, device=w.device)
+    _at_least(blocks, q4_0_nbytes(rows, cols), "blocks")
     _check("q4_0_pack", load_library().q4_0_pack(
         _dev(w, torch.float32, "w"), rows, cols, _dev(blocks, torch.uint8, "blocks"), _stream()))
     return blocks
@@ -359,10 +414,14 @@ def q4_0_pack(w, blocks=None):
 def cq_codebook_fit(samples, levels: int, iters: int = 200, table=None, raw=None):
     """Lloyd-Max fit on device fp64 samples -> (table fp32 [levels], raw fp64 [levels])."""
     torch = _torch()
+    if getattr(samples, "ndim", 0) != 1:
+        raise ValueError("samples must be 1-D")
     if table is None:
         table = torch.empty((levels,), dtype=torch.float32, device=samples.device)
     if raw is None:
         raw = torch.empty((levels,), dtype=torch.float64, device=samples.device)
+    _shape(table, (levels,), "table")
+    _shape(raw, (levels,), "raw")
     _check("cq_codebook_fit", load_library().cq_codebook_fit(
         _dev(samples, torch.float64, "samples"), samples.numel(), levels, iters,
         _dev(raw, torch.float64, "raw"), _dev(table, torch.float32, "table"), _stream()))

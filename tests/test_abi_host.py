@@ -119,6 +119,9 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.q4_0_gemm(p, 4, 312, None, 8, p, None) == E.BQM_EINVAL
     assert lib.q4_0_gemm(p, 4, 312, ctypes.c_void_p(4100), 8, p, None) == E.BQM_EALIGN
     assert lib.q4_0_gemm(p, 4, 1 << 20, p, 1024, p, None) == E.BQM_ENOTSUP     # m * cols * 4 >= 2^31
+    # q4_0_gemv addresses its blocks with 32-bit offsets: 2^27 rows of one block is past 2^31 bytes
+    assert lib.q4_0_gemv(p, 1 << 27, 32, p, 1, p, None) == E.BQM_ENOTSUP
+    assert lib.q4_0_gemv(p, (1 << 27) - 1, 1, ctypes.c_void_p(4100), 1, p, None) == E.BQM_ENOTSUP
     assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL
     assert lib.q4_0_pack(p, 0, 312, p, None) == E.BQM_EINVAL
     assert lib.cq_codebook_fit(p, 1 << 20, 16, 200, None, p, None) == E.BQM_ENOTSUP
@@ -132,3 +135,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library()
+
+
+def test_binding_checks_shapes_before_any_call(lib):
+    """Every wrapper compares each tensor with the layout / row and column
+    arguments and raises ValueError before a pointer reaches the library (CPU
+    tensors here: a call that passed the shape checks would stop at the device
+    check, whose message differs)."""
+    import torch
+
+    from bit_quantized_matmul_amd import binding as B
+    lay = B.cq_pack_info(64, 256, 128, 4)
+    cb = np.linspace(-1, 1, 16).astype(np.float32)
+    blob = torch.zeros(lay.total_bytes, dtype=torch.uint8)
+    q = torch.zeros((2, 256), dtype=torch.int8)
+    sc = torch.ones(2)
+    cases = [
+        (lambda: B.cq_gemv(blob, lay, cb, torch.zeros((2, 128), dtype=torch.int8), sc), "q must have shape"),
+        (lambda: B.cq_gemv(blob, lay, cb, q, torch.ones(3)), "scale must have shape"),
+        (lambda: B.cq_gemv(blob, lay, cb, q, sc, y=torch.zeros(2, 63)), "y must have shape"),
+        (lambda: B.cq_gemv(blob[:-64], lay, cb, q, sc), "blob must hold"),
+        (lambda: B.cq_gemv(blob, lay, cb[:8], q, sc), "codebook must hold"),
+        (lambda: B.cq_gemv(blob, lay, cb, q, sc), "CUDA/HIP tensor"),            # shapes right
+        (lambda: B.cq_gemm(blob, lay, cb, torch.zeros((5, 255), dtype=torch.int8), torch.ones(5)), "q must"),
+        (lambda: B.cq_gemm(blob, lay, cb, q, torch.ones(1)), "scale must have shape"),
+        (lambda: B.cq_gemv_f32(blob, lay, cb, torch.zeros(2, 512)), "x must have shape"),
+        (lambda: B.cq_gemv_f32(blob, lay, cb, torch.zeros(2, 256), q_out=torch.zeros((2, 255), dtype=torch.int8),
+                               scale_out=sc), "q_out must have shape"),
+        (lambda: B.cq_gemv_f32(blob, lay, cb, torch.zeros(2, 256), scale_out=torch.ones(4)), "scale_out must"),
+        (lambda: B.act_fwht_quant_a8(torch.zeros(2, 256), q=torch.zeros((2, 128), dtype=torch.int8)), "q must"),
+        (lambda: B.act_fwht_quant_a8(torch.zeros(256)), "x must be 2-D"),
+        (lambda: B.cq_pack(torch.zeros(64, 128), lay, cb), "w must have shape"),
+        (lambda: B.cq_pack(torch.zeros(64, 256), lay, cb, blob=blob[:100]), "blob must hold"),
+        (lambda: B.q4_0_gemv(torch.zeros(100, dtype=torch.uint8), 4, 312, torch.zeros(1, 312)), "blocks must hold"),
+        (lambda: B.q4_0_gemv(torch.zeros(4 * 10 * 18, dtype=torch.uint8), 4, 312, torch.zeros(1, 300)), "x must"),
+        (lambda: B.q4_0_gemv(torch.zeros(4 * 10 * 18, dtype=torch.uint8), 4, 312, torch.zeros(1, 312),
+                             y=torch.zeros(1, 5)), "y must have shape"),
+        (lambda: B.q4_0_gemm(torch.zeros(4 * 10 * 18, dtype=torch.uint8), 4, 312, torch.zeros(7, 311)), "x must"),
+        (lambda: B.q4_0_pack(torch.zeros(4, 312), blocks=torch.zeros(10, dtype=torch.uint8)), "blocks must"),
+        (lambda: B.cq_codebook_fit(torch.zeros(1000, dtype=torch.float64), 16, table=torch.zeros(8)), "table must"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
