@@ -33,20 +33,33 @@ def blocks_per_row(cols: int) -> int:
 
 
 def encode(w: np.ndarray) -> np.ndarray:
-    """fp32 W[rows, cols] -> uint8 [rows, nblk, 18] blocks."""
+    """fp32 W[rows, cols] -> uint8 [rows, nblk, 18] blocks.
+
+    Block b of a row covers columns 32b .. 32b+31; columns at or past ``cols``
+    are the zero padding of section 3.  Per block (section 2): the scale is
+    d = max|w| / 8 (1 for an all-zero block), stored as fp16 in bytes 0-1
+    (little-endian); element j gets q = round(w_j / d) clipped to [-8, 7] and
+    its nibble q + 8 goes to byte 2 + j // 2, in the low half for even j and
+    the high half for odd j."""
     w = np.asarray(w, dtype=np.float32)
     rows, cols = w.shape
-    pc = padded_cols(cols)
-    w2 = np.zeros((rows, pc), dtype=np.float32)
-    w2[:, :cols] = w
-    blk = w2.reshape(rows, pc // BLOCK, BLOCK)
-    amax = np.max(np.abs(blk), axis=-1)
-    d = np.where(amax > 0, amax / np.float32(8.0), np.float32(1.0)).astype(np.float32)
-    q = np.clip(np.rint(blk / d[..., None]), -8, 7)
-    nib = (q + 8).astype(np.uint8)
-    out = np.zeros((rows, pc // BLOCK, BLOCK_BYTES), dtype=np.uint8)
-    out[..., 0:2] = d.astype(np.float16)[..., None].view(np.uint8)
-    out[..., 2:] = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    nblk = blocks_per_row(cols)
+    out = np.zeros((rows, nblk, BLOCK_BYTES), dtype=np.uint8)
+    for b in range(nblk):
+        c0 = b * BLOCK
+        vals = np.zeros((rows, BLOCK), dtype=np.float32)          # the block's 32 weights, every row
+        width = min(BLOCK, cols - c0)
+        vals[:, :width] = w[:, c0:c0 + width]
+        amax = np.max(np.abs(vals), axis=1)
+        d = np.ones(rows, dtype=np.float32)
+        nz = amax > 0
+        d[nz] = amax[nz] / np.float32(8.0)                        # fp32, correctly rounded
+        bits = d.astype("<f2").view("<u2")
+        out[:, b, 0] = bits & 0xFF
+        out[:, b, 1] = bits >> 8
+        for j in range(BLOCK):
+            q = np.clip(np.rint(vals[:, j] / d), -8, 7).astype(np.int64)   # fp32 quotient, ties to even
+            out[:, b, 2 + j // 2] |= ((q + 8) << (4 * (j % 2))).astype(np.uint8)
     return out
 
 
