@@ -91,7 +91,7 @@ def weight_matrix_mixed(rng: np.random.Generator, rows: int, cols: int, group: i
     for period, f in MIXED_ROW_SCALES:
         w[r % period == period - 1] *= np.float32(f)
     if rows > 1 and cols > group:
-        g = w[1].reshape(-1, group)
+        g = w[1, :cols // group * group].reshape(-1, group)       # whole groups (a view of row 1)
         g[1::2] *= np.float32(1e-4)
     w[rows // 2] = 0.0
     return w
