@@ -22,7 +22,7 @@ GROUP = 128
 EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
     "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
-    "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data",
+    "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data", "cq_gemv_f32_noalloc",
 )
 KMCU_F32, KMCU_Q4 = 1, 2
 
@@ -90,6 +90,7 @@ def load_library() -> ctypes.CDLL:
         "act_fwht_quant_a8": ([P, I, I, I, P, P, P], I),
         "cq_gemv": ([P, LP, F, P, P, I, P, P], I),
         "cq_gemv_f32": ([P, LP, F, P, I, P, P, P, P], I),
+        "cq_gemv_f32_noalloc": ([P, LP, F, P, I, P, P], I),
         "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
         "q4_0_gemv": ([P, I, I, P, I, P, P], I),
         "q4_0_gemm": ([P, I, I, P, I, P, P], I),
@@ -247,6 +248,20 @@ def cq_gemv_f32(blob, layout: CqLayout, codebook, x, y=None, q_out=None, scale_o
     _check("cq_gemv_f32", load_library().cq_gemv_f32(
         _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(x, torch.float32, "x"),
         batch, _dev(y, torch.float32, "y"), qo, so, _stream()))
+    return y
+
+
+def cq_gemv_f32_noalloc(blob, layout: CqLayout, codebook, x, y):
+    """cq_gemv_f32 with the codes staged in the library's device scratch: the
+    call allocates nothing (y is the caller's)."""
+    torch = _torch()
+    batch = _rows2d(x, layout.cols, "x")
+    _at_least(blob, layout.total_bytes, "blob")
+    _shape(y, (batch, layout.rows), "y")
+    cb, _keep = _codebook_ptr(codebook, layout.levels)
+    _check("cq_gemv_f32_noalloc", load_library().cq_gemv_f32_noalloc(
+        _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(x, torch.float32, "x"),
+        batch, _dev(y, torch.float32, "y"), _stream()))
     return y
 
 

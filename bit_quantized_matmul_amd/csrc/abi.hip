@@ -158,6 +158,34 @@ int check_layout(const bqm_cq_layout *L) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? BQM_OK : BQM_EDEVICE; }
 
+// Scratch of cq_gemv_f32_noalloc: the int8 codes [batch, cols] and fp32
+// scales [batch] that cq_gemv_f32 stages in q_out / scale_out, for up to
+// kScratchBatch tokens of up to kScratchCols columns.  One copy per device
+// (each device holds its own, until the process ends).  Host code never
+// uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr int kScratchBatch = 16;
+constexpr int kScratchCols = 16384;
+constexpr size_t kScratchCodes = (size_t)kScratchBatch * kScratchCols;   // 256 KiB of codes
+constexpr size_t kScratchBytes = kScratchCodes + 256;                     // + the scales
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+uint8_t *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(uint8_t **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BQM_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return BQM_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BQM_EDEVICE;
+    g_scratch[dev] = static_cast<uint8_t *>(p);
+  }
+  *out = g_scratch[dev];
+  return BQM_OK;
+}
+
 }  // namespace
 }  // namespace bqm
 
@@ -264,6 +292,24 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
   }
   return status_of(launch_cq_gemv_f32((const uint8_t *)blob, *layout, T, x, batch, y, q_out,
                                       scale_out, cus, (hipStream_t)stream));
+}
+
+int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+                        const float *x, int batch, float *y, bqm_stream_t stream) {
+  if (!blob || !x || !y || batch < 1) return BQM_EINVAL;
+  const int rc = check_layout(layout);
+  if (rc) return rc;
+  if (batch > kScratchBatch || layout->cols > kScratchCols) return BQM_ENOTSUP;   // past the scratch
+  int cus;
+  int rd = current_device(&cus);
+  if (rd) return rd;
+  uint8_t *sp = nullptr;
+  rd = scratch_of_current_device(&sp);
+  if (rd) return rd;
+  // the codes at the start of the scratch, the scales 256-byte aligned after
+  // the largest code block
+  return cq_gemv_f32(blob, layout, codebook, x, batch, y, reinterpret_cast<int8_t *>(sp),
+                     reinterpret_cast<float *>(sp + kScratchCodes), stream);
 }
 
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook, const int8_t *q,

@@ -145,6 +145,22 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);
 
+/* cq_gemv_f32 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Computes exactly what cq_gemv_f32 computes with q_out and scale_out given
+ * (same routes, same kernels, bit-identical y), but stages the int8 codes
+ * and scales in a library-owned device scratch instead of caller buffers:
+ * 256 KiB + 256 bytes per device, a static device array that each device
+ * holds until the process ends (its address is looked up once per device, on
+ * the first call there).  The call itself allocates nothing.  Limits: batch
+ * <= 16 and cols <= 16384 (BQM_ENOTSUP past them), otherwise those of
+ * cq_gemv_f32.  Every call on a device shares that device's scratch: calls
+ * that may overlap on one device (different streams without ordering, or
+ * host threads) race and must be serialized by the caller.  The scratch
+ * needs no clearing: each call writes all it reads. */
+int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const float *codebook,
+                        const float *x, int batch, float *y, bqm_stream_t stream);
+
 /* Prefill GEMM on packed CQ weights (Needle article, section 3: prefill is a
  * GEMM with the same layout, every row one reduction stream).  Same sum as
  * cq_gemv for m tokens: q [device] int8 [m, cols], scale [device] fp32 [m],
