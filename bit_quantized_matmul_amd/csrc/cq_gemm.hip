@@ -18,8 +18,8 @@
 //    the group's norm times 2^e_n with one packed fp16 multiply.  e_n is an
 //    exponent per weight row n, chosen from the row's largest norm so that
 //    level x norm x 2^e_n stays below 2^15 for every level and group of the
-//    row; norm x 2^e_n is formed exactly in fp32 and converted exactly to
-//    fp16.  The packed multiply is then the one rounding of the path: at most
+//    row; norm x 2^e_n is formed exactly with one v_ldexp_f16.  The packed
+//    multiply is then the one rounding of the path: at most
 //    2^-11 relative per weight for every group whose products stay in fp16's
 //    normal range, i.e. whose norm is at least ~2^-23 of the row's largest
 //    (smaller groups round to fp16 subnormals, an absolute error below
@@ -356,7 +356,8 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // e_n = fold_exp - E_M with E_M = floor(log2(largest norm)): then
   // norm x 2^e_n < 2^15 and level x norm x 2^e_n < 2^15 for every level
   // (fold_exp = 13 - max(floor(log2(largest |level|)), -1), from the host)
-  float rsc[NB], rinv[NB];                         // 2^e_n and 2^-e_n
+  int rexp[NB];                                    // e_n
+  float rinv[NB];                                  // 2^-e_n
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const uint32_t hm = max(nmax[nb], (uint32_t)__shfl_xor((int)nmax[nb], 32, 64));
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     else if (hm >= 0x7C00u) e = -2;                // inf / NaN norms: no scaling can help
     else if (hm >= 0x400u) e = T.fold_exp - ((int)(hm >> 10) - 15);
     else e = T.fold_exp - ((31 - __builtin_clz(hm)) - 24);   // subnormal largest norm
-    rsc[nb] = __uint_as_float((uint32_t)(127 + e) << 23);
+    rexp[nb] = e;
     rinv[nb] = __uint_as_float((uint32_t)(127 - e) << 23);
   }
 
@@ -396,7 +397,9 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     }
     return o;
   };
-  // group g's norm x 2^e_n as an fp16 pair (formed exactly in fp32): from
+  // group g's norm x 2^e_n as an fp16 pair (v_ldexp_f16: exact, since the
+  // result is at most 2^15 and, but for groups far below the row's largest,
+  // normal; groups past K get 2^-64, i.e. zero): from
   // prefetch slot d, or (N8) from this loop round's or the next one's norms,
   // where group g is halfword g % 8
   auto take_group = [&](int g, int d, bool next) {
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
       } else {
         nw = npre[d][nb] >> ((((uint32_t)(ncol[nb] * ng + kgroup(g))) & 1u) * 16u);
       }
-      const _Float16 h = (_Float16)(half_bits_to_float((uint16_t)nw) * (g < ng ? rsc[nb] : 0.0f));
+      const _Float16 h = __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)nw), g < ng ? rexp[nb] : -64);
       nq[nb] = h2v{h, h};
     }
   };
