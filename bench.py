@@ -19,7 +19,8 @@ bit-width sweep, the same decode layer shapes at 4 and
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|floor|copy   (profiling runs)
+       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|floor|copy|c1
+       (profiling runs)
 """
 from __future__ import annotations
 
@@ -56,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "q4_0_prefill", "sweep",
-                                       "batched", "kmcu", "floor", "copy"])
+                                       "batched", "kmcu", "floor", "copy", "c1"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -117,6 +118,38 @@ def graph_mean_ms(torch, launches, reps: int = 3) -> float:
     ms = s.elapsed_time(e) / (reps * len(launches))
     del g
     return ms
+
+
+def graph_repeats_ms(torch, launches, repeats: int = 5) -> list:
+    """Per-launch mean of `launches` captured once in a HIP graph, for each of
+    `repeats` separate replays (each replay timed alone between a HIP event
+    pair on the launch stream)."""
+    for fn in launches[:2]:
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in launches:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e) / len(launches))
+    del g
+    return out
+
+
+def spread(values_ms, scale=1e3) -> dict:
+    """min / median / max of repeated timings (ms -> us by default)."""
+    v = sorted(x * scale for x in values_ms)
+    return dict(min=v[0], median=v[len(v) // 2], max=v[-1], n=len(v))
 
 
 def pool_copies(nbytes: int, minimum: int = 2) -> int:
@@ -201,9 +234,11 @@ def bench_decode(B, torch, dev, cbs, steps, warmup):
                 step_fn(B, mats, pool, slot, cb4)
         return g
 
-    def per_step_ms(step_fn, slots_of):
+    def per_step_ms(step_fn, slots_of, repeats=1):
         """W untimed warm-up steps, then exactly K timed steps, each run as one
-        graph replay; slots_of(i) is step i's weight copy."""
+        graph replay; slots_of(i) is step i's weight copy.  With repeats > 1
+        the same K steps are timed again (each replay alone): the list of
+        per-step times is returned, the first being the contract's run."""
         if warmup:
             gw = graph_of(step_fn, [slots_of(i) for i in range(warmup)])
             gw.replay()
@@ -211,21 +246,25 @@ def bench_decode(B, torch, dev, cbs, steps, warmup):
             del gw
         g = graph_of(step_fn, [slots_of(warmup + i) for i in range(steps)])
         torch.cuda.synchronize()
-        t = Timer()
-        t.start()
-        g.replay()
-        ms = t.stop_ms() / steps
+        times = []
+        for _ in range(repeats):
+            t = Timer()
+            t.start()
+            g.replay()
+            times.append(t.stop_ms() / steps)
         del g
-        return ms
+        return times if repeats > 1 else times[0]
 
-    # HBM-cold: the weight copies cycled in order, one per step
-    ms = per_step_ms(run_step, lambda i: i % ncopies)
+    # HBM-cold: the weight copies cycled in order, one per step; the first
+    # timed run is the headline, four more give the spread
+    reps = per_step_ms(run_step, lambda i: i % ncopies, repeats=5)
+    ms = reps[0]
     # warm: the same copy every step (its weights stay in the Infinity Cache)
     ms_warm = per_step_ms(run_step, lambda i: 0)
     # the two-launch variant of the step (A8 and GEMV as separate kernels)
     ms_two = per_step_ms(run_step_two_launch, lambda i: i % ncopies)
     torch.cuda.synchronize()
-    res = dict(ms_per_step=ms, step_bytes=step_bytes, pool_copies=ncopies,
+    res = dict(ms_per_step=ms, step_us_repeats=spread(reps), step_bytes=step_bytes, pool_copies=ncopies,
                gbps=step_bytes / ms / 1e6, ms_two_launch=ms_two,
                gbps_two_launch=step_bytes / ms_two / 1e6, ms_warm=ms_warm,
                gbps_warm_infinity_cache=step_bytes / ms_warm / 1e6)
@@ -254,15 +293,42 @@ def bench_dominant(B, torch, dev, cbs, steps, mats=None, pool=None):
     m = mats[i]
     cp = cold_pool(pool[i][0], pool[i])
     n = max(2 * len(cp), steps)
-    reps = 3
-    d_ms = graph_mean_ms(torch, [
+    times = graph_repeats_ms(torch, [
         (lambda k=k: B.cq_gemv_f32(cp[k % len(cp)], m["lay"], cbs[4], m["x"], y=m["y"]))
-        for k in range(n)], reps=reps)
+        for k in range(n)], repeats=5)
+    d_ms = sorted(times)[len(times) // 2]                               # the median replay
     lay = m["lay"]
     algo = payload_bytes(lay) + lay.cols * 4 + lay.rows * 4           # weights + fp32 x + fp32 y
     return dict(kernel="cq_gemv_kernel, fused A8 (cq_gemv_f32: CQ 4-bit GEMV, 4096x14336, batch 1)",
-                avg_us=d_ms * 1e3, launches=n * reps, algo_bytes=algo,
+                avg_us=d_ms * 1e3, us_repeats=spread(times), launches=n * len(times), algo_bytes=algo,
                 achieved_gbps=algo / d_ms / 1e6)
+
+
+def bench_c1(B, torch, dev, cbs):
+    """The single CQ-W4A8 GEMV: 512x512 cb4, batch 1 (one cq_gemv_f32 launch,
+    135 KB of weights: launch-bound).  Graph-timed warm (one copy) and
+    HBM-cold (cycling >= 1 GiB of copies); y is returned for the parity check
+    in the cpu_baseline leg."""
+    from bit_quantized_matmul_amd import inputs
+    wl = inputs.cq_single()
+    w, xh = wl.weights[0][1], wl.acts[0]
+    lay = B.cq_pack_info(512, 512, 128, 4)
+    blob = B.cq_pack(torch.from_numpy(w).to(dev), lay, cbs[4])
+    x = torch.from_numpy(xh).to(dev)
+    y = torch.empty((1, 512), dtype=torch.float32, device=dev)
+    warm = graph_repeats_ms(torch, [(lambda: B.cq_gemv_f32(blob, lay, cbs[4], x, y=y)) for _ in range(100)])
+    pool = cold_pool(blob)
+    cold = graph_repeats_ms(torch, [(lambda k=k: B.cq_gemv_f32(pool[k], lay, cbs[4], x, y=y))
+                                    for k in range(len(pool))], repeats=3)
+    B.cq_gemv_f32(blob, lay, cbs[4], x, y=y)
+    torch.cuda.synchronize()
+    nb = payload_bytes(lay)
+    d = sorted(cold)[1]
+    res = dict(workload="cq_single_512x512_b1 (cb4, group 128, fp32 x -> A8 fused)", bytes=nb,
+               us_warm=spread(warm), us_hbm_cold=spread(cold), gbps_hbm_cold=nb / d / 1e6,
+               pool_copies=len(pool))
+    del pool
+    return res, dict(w=w, x=xh, y=y.cpu().numpy(), blob=blob.cpu().numpy())
 
 
 def bench_read_floor(torch, dev, rows: int = 4096, cols: int = 1852):
@@ -299,13 +365,13 @@ def bench_prefill(B, torch, dev, cbs, steps, warmup):
         y = torch.empty((q.shape[0], rows), dtype=torch.float32, device=dev)
         for _ in range(warmup):
             B.cq_gemm(blob, lay, cbs[4], q, s, y=y)
-        t.start()
-        for _ in range(steps):
-            B.cq_gemm(blob, lay, cbs[4], q, s, y=y)
-        ms = t.stop_ms() / steps
+        times = graph_repeats_ms(torch, [(lambda: B.cq_gemm(blob, lay, cbs[4], q, s, y=y))
+                                         for _ in range(max(steps, 10))], repeats=5)
+        ms = sorted(times)[len(times) // 2]
         flops = 2.0 * q.shape[0] * rows * cols
         tf = flops / ms / 1e9
-        out[label] = dict(m=int(q.shape[0]), us=ms * 1e3, tflops=tf, frac=tf / MFMA_F16_PEAK_TFLOPS)
+        out[label] = dict(m=int(q.shape[0]), us=ms * 1e3, us_repeats=spread(times), tflops=tf,
+                          frac=tf / MFMA_F16_PEAK_TFLOPS)
         del blob, y
     # context: the dense fp16 GEMM the format avoids (hipBLASLt via torch.mm,
     # contiguous [M, K] x [K, N] operands, fp16 weights of the same shape)
@@ -362,9 +428,34 @@ def bench_q4_0(B, torch, dev, steps, warmup):
     # graph-timed: eager launches from Python are host-bound at this size
     rows, cols, blocks, x, y = items[-1]
     ms_head = graph_mean_ms(torch, [(lambda: B.q4_0_gemv(blocks, rows, cols, x, y=y)) for _ in range(max(steps, 20))])
+    # HBM-cold: >= 1 GiB of distinct copies of the whole pass, one graph of
+    # consecutive passes each on the next copy (the 256 MB Infinity Cache
+    # cannot hold them); the head alone likewise over its own pool
+    ncop = pool_copies(total)
+    copies = [[it[2]] + [it[2].clone() for _ in range(ncop - 1)] for it in items]
+    torch.cuda.synchronize()
+
+    def cold_pass(k):
+        for i, (r_, c_, _, x_, y_) in enumerate(items):
+            B.q4_0_gemv(copies[i][k], r_, c_, x_, y=y_)
+
+    cold = graph_repeats_ms(torch, [(lambda k=k: cold_pass(k)) for k in range(ncop)], repeats=3)
+    ms_cold = sorted(cold)[1]
+    head_pool = copies[-1] + [blocks.clone() for _ in range(max(0, pool_copies(blocks.numel()) - ncop))]
+    hc = graph_repeats_ms(torch, [(lambda k=k: B.q4_0_gemv(head_pool[k], rows, cols, x, y=y))
+                                  for k in range(len(head_pool))], repeats=3)
+    ms_head_cold = sorted(hc)[1]
+    del copies, head_pool
+    torch.cuda.synchronize()
     return dict(launches=len(items), bytes=total, us_graph=ms * 1e3, gbps_graph=total / ms / 1e6,
                 us_eager=ms_eager * 1e3, head_us=ms_head * 1e3,
-                head_gbps=blocks.numel() / ms_head / 1e6, note="weights in Infinity Cache (13 MB pass)")
+                head_gbps=blocks.numel() / ms_head / 1e6,
+                note="us_graph / head_us: weights warm in the Infinity Cache (the 13 MB pass fits); "
+                     "*_hbm_cold: cycling >= 1 GiB of copies",
+                pass_us_hbm_cold=ms_cold * 1e3, pass_gbps_hbm_cold=total / ms_cold / 1e6,
+                pass_copies=ncop, head_us_hbm_cold=ms_head_cold * 1e3,
+                head_gbps_hbm_cold=blocks.numel() / ms_head_cold / 1e6,
+                head_frac_hbm_cold=blocks.numel() / ms_head_cold / 1e6 / HBM_PEAK_GBPS)
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
@@ -555,10 +646,31 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(reps: int = 60, rows_per_matrix: int = 512):
+def c1_parity(c1, matmul, cq, a8, codebook):
+    """The C1 GEMV's device result against the oracle, element by element:
+    the oracle fits the codebook on the same samples and encodes W itself
+    (its blob must equal the device's); the error is stated as
+    max |y - ref| / magnitude and relative L2."""
+    from bit_quantized_matmul_amd import inputs
+    lv = codebook.shipped_table(codebook.lloyd_max_fit(inputs.gaussian_samples(), 16))
+    idx, n16 = cq.encode(c1["w"], 128, 4, lv)
+    blob_ok = bool(np.array_equal(cq.make_blob(idx, n16, 128, 4), c1["blob"]))
+    q, s = a8.act_quant_a8(c1["x"], 128, "fp32")
+    t0 = time.perf_counter()
+    ref = matmul.cq_reference(idx, n16, 128, 4, lv, q, s)
+    oracle_s = time.perf_counter() - t0
+    mag = matmul.cq_magnitude(idx, n16, 128, 4, lv, q, s)
+    err = np.abs(c1["y"].astype(np.float64) - ref)
+    return dict(blob_bit_exact=blob_ok, max_err_over_magnitude=float(np.max(err / mag)),
+                bound=1e-5, rel_l2=matmul.rel_l2(c1["y"], ref), max_abs_err=float(err.max()),
+                oracle_product_ms=oracle_s * 1e3)
+
+
+def cpu_baseline(reps: int = 60, rows_per_matrix: int = 512, c1=None):
     """The oracle (unchanged) on a bounded sample of the decode step: the
     plain definition (the reported value), the rotated-domain form, and the
-    plain definition on one thread."""
+    plain definition on one thread.  With `c1` (the 512x512 GEMV's device
+    result) it also checks that result against the oracle."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from bit_quantized_matmul_amd import inputs
@@ -588,7 +700,9 @@ def cpu_baseline(reps: int = 60, rows_per_matrix: int = 512):
     one_reps = max(1, reps // 10)
     with threadpool_limits(limits=1):
         dt_one = timed(matmul.cq_reference, one_reps)
+    c1_check = None if c1 is None else c1_parity(c1, matmul, cq, a8, codebook)
     return dict(value=reps * nbytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                c1_parity=c1_check,
                 seconds=dt,
                 sample=f"first {rows_per_matrix} rows of each decode matrix (4096x4096, 1024x4096, "
                        f"14336x4096, 4096x14336), oracle A8 + plain-definition product "
@@ -669,6 +783,9 @@ def main():
     if args.only == "batched":
         print(json.dumps(bench_batched(B, torch, dev, cbs, args.steps)))
         return
+    if args.only == "c1":
+        print(json.dumps(bench_c1(B, torch, dev, cbs)[0]))
+        return
 
     dec, mats, pool = bench_decode(B, torch, dev, cbs, args.steps, args.warmup)
     log(f"decode step {dec['ms_per_step'] * 1e3:.1f} us, {dec['gbps']:.0f} GB/s")
@@ -696,7 +813,9 @@ def main():
     km = bench_kmcu_load(B, torch, dev, args.steps)
     log(f"kmcu load: {km['file_mib']:.2f} MiB image, pinned {km['pinned_gbps']:.1f} GB/s, "
         f"pageable {km['pageable_gbps']:.1f} GB/s")
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    c1, c1_data = bench_c1(B, torch, dev, cbs)
+    log(f"C1 512x512: {c1['us_warm']['median']:.2f} us warm, {c1['us_hbm_cold']['median']:.2f} us HBM-cold")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(c1=c1_data)
     if cpu:
         log(f"cpu baseline {cpu['value']:.4f} GB/s in {cpu['seconds']:.1f} s")
 
@@ -736,6 +855,7 @@ def main():
             "traffic": traffic,
             "algo_bytes_per_launch": dom["algo_bytes"],
             "avg_launch_us": round(dom["avg_us"], 3),
+            "launch_us_repeats": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in dom["us_repeats"].items()},
         },
         "cpu_baseline": (None if cpu is None else
                          {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cpu.items()}),
@@ -748,6 +868,7 @@ def main():
         "batched_decode_cb4": bat,
         "kmcu_load_minueza_tied": km,
         "hbm_read_floor_30MB": floor,
+        "c1_single_512x512": c1,
     }
     print(json.dumps(line))
 
