@@ -15,6 +15,11 @@ values x_u = H_u x_g (unnormalized), s = max|x_u| / 127 over the whole row
 Two modes: ``fp32`` performs every step in fp32 with the same butterfly
 network and a correctly rounded fp32 division, so its q is the one and only
 right answer for a device that does the same; ``fp64`` is the exact math.
+
+``act_quant_a8_unrotated`` is the same per-token quantizer without the
+rotation, for the Q4_0 format, which carries no Hadamard rotation (the
+Minueza-32M -> KMCU v1 page, sections 2-3): its group is 1, and the
+transform of length 1 is the identity.
 """
 from __future__ import annotations
 
@@ -43,6 +48,12 @@ def act_quant_a8(x: np.ndarray, group: int, mode: str = "fp32"):
     r = np.rint(u / s[:, None])          # division in dt, correctly rounded
     q = np.clip(r, -QMAX, QMAX).astype(np.int8)
     return q, s
+
+
+def act_quant_a8_unrotated(x: np.ndarray, mode: str = "fp32"):
+    """Per-token symmetric int8 of x itself: s = max|x| / 127 over the row
+    (1 for an all-zero row), q = clip(rint(x / s), -127, 127)."""
+    return act_quant_a8(x, 1, mode)
 
 
 def dequant_a8(q: np.ndarray, s: np.ndarray, group: int) -> np.ndarray:

@@ -69,6 +69,18 @@ def q4_0_magnitude(blocks, cols, x) -> np.ndarray:
     return np.abs(np.asarray(x, dtype=np.float64)) @ np.abs(w_hat).T
 
 
+def q4_0_a8_reference(blocks, cols, q, s) -> np.ndarray:
+    """Q4_0 weights against int8 activations: y[b, r] = s_b * sum_k W_hat[r, k] * q[b, k],
+    fp64 (the plain definition on the decoded operands, x_hat = s * q)."""
+    x_hat = np.asarray(q, dtype=np.float64) * np.asarray(s, dtype=np.float64)[:, None]
+    return q4_0_reference(blocks, cols, x_hat)
+
+
+def q4_0_a8_magnitude(blocks, cols, q, s) -> np.ndarray:
+    x_hat = np.asarray(q, dtype=np.float64) * np.asarray(s, dtype=np.float64)[:, None]
+    return q4_0_magnitude(blocks, cols, x_hat)
+
+
 def rel_l2(y, ref) -> float:
     """||y - ref||_2 / ||ref||_2 (the tolerance measure); 0-norm ref -> abs."""
     y = np.asarray(y, dtype=np.float64)

@@ -91,6 +91,28 @@ def test_a8_ties_round_half_to_even(mode):
         assert np.array_equal(q[0].astype(np.int64), q_want)
 
 
+@pytest.mark.parametrize("mode", ["fp32", "fp64"])
+def test_a8_unrotated_ties_and_range(mode):
+    """Without the rotation the hand-built rotated values are the activations
+    themselves (H of length 1 is the identity): the same hand-worked codes."""
+    g = {r[0].split(":", 1)[0]: r[0].split(":", 1)[1].strip() for r in read_golden_rows("a8_ties.txt")}
+    for r in range(2):
+        x = _sparse(g[f"row{r}_u"]).astype(np.float32)
+        q, s = a8.act_quant_a8_unrotated(x[None, :], mode)
+        assert float(s[0]) == float(g[f"row{r}_s"])
+        assert np.array_equal(q[0].astype(np.int64), _sparse(g[f"row{r}_q"]).astype(np.int64))
+    # a zero row, the amax element at +-127, |x - s q| <= s / 2, odd widths
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((3, 1092)).astype(np.float32)
+    x[1] = 0
+    q, s = a8.act_quant_a8_unrotated(x, mode)
+    assert np.all(q[1] == 0) and s[1] == 1
+    for r in (0, 2):
+        k = int(np.argmax(np.abs(x[r])))
+        assert abs(int(q[r, k])) == 127
+        assert np.all(np.abs(x[r].astype(np.float64) - float(s[r]) * q[r]) <= 0.5 * float(s[r]) * (1 + 1e-6))
+
+
 # --------------------------------------------------------------------- Q4_0
 
 def test_q4_0_hand_built_block():
@@ -280,3 +302,24 @@ def test_q4_0_magnitude_bounds_and_equality():
     blp = q4_0.encode(wp)
     xp = np.abs(x)
     assert np.allclose(matmul.q4_0_magnitude(blp, 70, xp), matmul.q4_0_reference(blp, 70, xp), rtol=1e-12)
+
+
+def test_q4_0_a8_reference_brute_force():
+    """Q4_0 weights x int8 codes: a scalar loop over the blocks' bytes."""
+    rng = np.random.default_rng(51)
+    w = (0.02 * rng.standard_normal((3, 45))).astype(np.float32)
+    x = rng.standard_normal((2, 45)).astype(np.float32)
+    blk = q4_0.encode(w)
+    q, s = a8.act_quant_a8_unrotated(x)
+    ref = np.zeros((2, 3))
+    for b in range(2):
+        for r in range(3):
+            for k in range(45):
+                byte = blk[r, k // 32, 2 + (k % 32) // 2]
+                nib = (byte >> 4) if k % 2 else (byte & 0xF)
+                d = float(blk[r, k // 32, 0:2].view(np.float16)[0])
+                ref[b, r] += (int(nib) - 8) * d * int(q[b, k])
+            ref[b, r] *= float(s[b])
+    assert np.max(np.abs(matmul.q4_0_a8_reference(blk, 45, q, s) - ref)) < 1e-15 * max(1.0, np.abs(ref).max())
+    mag = matmul.q4_0_a8_magnitude(blk, 45, q, s)
+    assert np.all(np.abs(ref) <= mag * (1 + 1e-12))
