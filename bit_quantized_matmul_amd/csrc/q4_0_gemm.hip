@@ -189,9 +189,13 @@ hipError_t launch_q4_0_gemm(const uint8_t *blocks, int rows, int cols, const flo
   const int tm = split ? 32 : kTileM, tn = split ? 32 : kTileN;
   const dim3 grid((rows + tn - 1) / tn, (m + tm - 1) / tm);
   if (grid.y > 65535) return hipErrorInvalidValue;
+  // the blocks' range in whole dwords: a dword load that reaches past the
+  // range reads zero as a whole, which would drop the last 2 nibble bytes of
+  // the last block when it starts 4-byte aligned (the 1-3 bytes beyond share
+  // a dword, hence a page, with the last valid bytes and are never used)
+  const uint32_t range = (uint32_t)((block_bytes + 3) & ~(size_t)3);
   auto go = [&](auto kern) {
-    kern<<<grid, kGemmThreads, 0, s>>>(blocks, rows, cols, nblk, (uint32_t)block_bytes, x, (uint32_t)x_bytes,
-                                       m, y);
+    kern<<<grid, kGemmThreads, 0, s>>>(blocks, rows, cols, nblk, range, x, (uint32_t)x_bytes, m, y);
   };
   if ((cols & 3) == 0) {
     if (split) go(q4_0_gemm_kernel<true, 4>);

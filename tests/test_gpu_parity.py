@@ -276,7 +276,10 @@ def test_q4_0_gemv_parity(rows, cols, batch):
 # the 4-byte activation loads), single rows, tokens and columns
 @pytest.mark.parametrize("rows,cols,m", [(312, 312, 37), (104, 312, 512), (1092, 312, 64),
                                          (312, 1092, 100), (32002, 312, 130), (70, 33, 65),
-                                         (129, 101, 3), (1, 1, 1), (5, 64, 1)])
+                                         (129, 101, 3), (1, 1, 1), (5, 64, 1),
+                                         # an odd block count with a full last block: that
+                                         # block starts 4-byte aligned and ends the buffer
+                                         (1, 96, 5), (3, 32, 7), (7, 160, 33)])
 def test_q4_0_gemm_parity(rows, cols, m):
     rng = np.random.default_rng(650 + rows + cols + m)
     w = inputs.weight_matrix(rng, rows, cols)
