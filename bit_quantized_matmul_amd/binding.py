@@ -23,6 +23,7 @@ EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
     "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
     "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data", "cq_gemv_f32_noalloc",
+    "q4_0_gemv_a8", "q4_0_gemm_a8",
 )
 KMCU_F32, KMCU_Q4 = 1, 2
 
@@ -94,6 +95,8 @@ def load_library() -> ctypes.CDLL:
         "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
         "q4_0_gemv": ([P, I, I, P, I, P, P], I),
         "q4_0_gemm": ([P, I, I, P, I, P, P], I),
+        "q4_0_gemv_a8": ([P, I, I, P, P, I, P, P], I),
+        "q4_0_gemm_a8": ([P, I, I, P, P, I, P, P], I),
         "cq_pack": ([P, LP, F, P, P, P], I),
         "q4_0_pack": ([P, I, I, P, P], I),
         "cq_codebook_fit": ([P, I64, I, I, P, P, P], I),
@@ -307,6 +310,30 @@ def q4_0_gemm(blocks, rows: int, cols: int, x, y=None):
         _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), m,
         _dev(y, torch.float32, "y"), _stream()))
     return y
+
+
+def _q4_0_a8(fn, blocks, rows, cols, q, scale, y):
+    torch = _torch()
+    n = _rows2d(q, cols, "q")
+    _at_least(blocks, q4_0_nbytes(rows, cols), "blocks")
+    _shape(scale, (n,), "scale")
+    if y is None:
+        y = torch.empty((n, rows), dtype=torch.float32, device=q.device)
+    _shape(y, (n, rows), "y")
+    _check(fn, getattr(load_library(), fn)(
+        _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(q, torch.int8, "q"),
+        _dev(scale, torch.float32, "scale"), n, _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def q4_0_gemv_a8(blocks, rows: int, cols: int, q, scale, y=None):
+    """Q4_0 blocks x int8 codes q [batch, cols] (act_fwht_quant_a8, group 1) -> fp32 y [batch, rows]."""
+    return _q4_0_a8("q4_0_gemv_a8", blocks, rows, cols, q, scale, y)
+
+
+def q4_0_gemm_a8(blocks, rows: int, cols: int, q, scale, y=None):
+    """Q4_0 blocks x int8 codes q [m, cols] -> fp32 y [m, rows] on the int8 matrix cores."""
+    return _q4_0_a8("q4_0_gemm_a8", blocks, rows, cols, q, scale, y)
 
 
 # ---------------------------------------------------------------- KMCU container

@@ -230,13 +230,14 @@ int cq_analytic_levels(int bits, float *levels) {
 
 int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float *scale,
                       bqm_stream_t stream) {
-  if (!x || !q || !scale || m < 1 || k < 1 || group < 2 || (group & (group - 1))) return BQM_EINVAL;
+  if (!x || !q || !scale || m < 1 || k < 1 || group < 1 || (group & (group - 1))) return BQM_EINVAL;
   if (k % group) return BQM_EINVAL;
-  if (group != kGroup || k > 65536) return BQM_ENOTSUP;
+  if ((group != kGroup && group != 1) || k > 65536) return BQM_ENOTSUP;
   if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scale & 3u)) return BQM_EALIGN;
   int cus;
   const int rc = current_device(&cus);
   if (rc) return rc;
+  if (group == 1) return status_of(launch_act_quant_a8_unrotated(x, m, k, q, scale, (hipStream_t)stream));
   return status_of(launch_act_fwht_quant_a8(x, m, k, q, scale, (hipStream_t)stream));
 }
 
@@ -360,6 +361,34 @@ int q4_0_gemm(const void *blocks, int rows, int cols, const float *x, int m, flo
   const int rc = current_device(&cus);
   if (rc) return rc;
   return status_of(launch_q4_0_gemm((const uint8_t *)blocks, rows, cols, x, m, y, cus, (hipStream_t)stream));
+}
+
+int q4_0_gemv_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int batch,
+                 float *y, bqm_stream_t stream) {
+  if (!blocks || !q || !scale || !y || rows < 1 || cols < 1 || batch < 1) return BQM_EINVAL;
+  // 32-bit offsets for the blocks and the codes
+  if (batch > 16 || (int64_t)rows * (((int64_t)cols + 31) / 32) * 18 >= ((int64_t)1 << 31) ||
+      (int64_t)batch * cols >= ((int64_t)1 << 31))
+    return BQM_ENOTSUP;
+  if (!aligned16(blocks) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_q4_0_gemv_a8((const uint8_t *)blocks, rows, cols, q, scale, batch, y, (hipStream_t)stream));
+}
+
+int q4_0_gemm_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int m, float *y,
+                 bqm_stream_t stream) {
+  if (!blocks || !q || !scale || !y || rows < 1 || cols < 1 || m < 1) return BQM_EINVAL;
+  if ((int64_t)rows * (((int64_t)cols + 31) / 32) * 18 >= ((int64_t)1 << 31) ||
+      (int64_t)m * cols >= ((int64_t)1 << 31) || ((int64_t)m + 31) / 32 > 65535)
+    return BQM_ENOTSUP;
+  if (!aligned16(blocks) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_q4_0_gemm_a8((const uint8_t *)blocks, rows, cols, q, scale, m, y, cus,
+                                       (hipStream_t)stream));
 }
 
 int cq_pack(const float *w, const bqm_cq_layout *layout, const float *codebook, void *blob,

@@ -152,7 +152,63 @@ __global__ __launch_bounds__(kThreads) void act_fwht_quant_a8_kernel(
   }
 }
 
+// Group 1: the same per-token quantizer without the rotation (the transform
+// of length 1 is the identity), for the Q4_0 products, whose weights carry no
+// rotation.  k is any length (Q4_0 rows need not fill a 128-group): element i
+// of the row belongs to thread i % kThreads.  s = max|x| / 127 (1 for a zero
+// row), q = clip(rint(x / s), -127, 127), both divisions correctly rounded.
+template <int EPT, int kThreads>
+__global__ __launch_bounds__(kThreads) void act_quant_a8_unrotated_kernel(
+    const float *__restrict__ x, int k, int8_t *__restrict__ q, float *__restrict__ scale) {
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const float *xr = x + (size_t)row * k;
+  float v[EPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = t + e * kThreads;
+    v[e] = i < k ? xr[i] : 0.0f;
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+  __shared__ float red[kThreads / kWave];
+  __shared__ float s_shared;
+  amax = wave_max_dpp(amax);
+  if ((t & 63) == 63) red[t >> 6] = amax;
+  __syncthreads();
+  if (t == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) m = fmaxf(m, red[w]);
+    const float s = (m > 0.0f) ? div_rn(m, 127.0f) : 1.0f;
+    s_shared = s;
+    scale[row] = s;
+  }
+  __syncthreads();
+  const float s = s_shared;
+  int8_t *qr = q + (size_t)row * k;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = t + e * kThreads;
+    if (i < k) {
+      const float r = fminf(fmaxf(rintf(div_rn(v[e], s)), -127.0f), 127.0f);
+      qr[i] = (int8_t)(int)r;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_act_quant_a8_unrotated(const float *x, int m, int k, int8_t *q, float *scale,
+                                         hipStream_t s) {
+  const dim3 grid(m);
+  if (k <= 256) act_quant_a8_unrotated_kernel<1, 256><<<grid, 256, 0, s>>>(x, k, q, scale);
+  else if (k <= 1024) act_quant_a8_unrotated_kernel<1, 1024><<<grid, 1024, 0, s>>>(x, k, q, scale);
+  else if (k <= 4096) act_quant_a8_unrotated_kernel<4, 1024><<<grid, 1024, 0, s>>>(x, k, q, scale);
+  else if (k <= 16384) act_quant_a8_unrotated_kernel<16, 1024><<<grid, 1024, 0, s>>>(x, k, q, scale);
+  else act_quant_a8_unrotated_kernel<64, 1024><<<grid, 1024, 0, s>>>(x, k, q, scale);   // k <= 65536
+  return hipGetLastError();
+}
 
 hipError_t launch_act_fwht_quant_a8(const float *x, int m, int k, int8_t *q, float *scale,
                                     hipStream_t s) {

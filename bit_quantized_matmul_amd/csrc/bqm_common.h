@@ -106,6 +106,12 @@ namespace bqm {
 
 hipError_t launch_act_fwht_quant_a8(const float *x, int m, int k, int8_t *q, float *scale,
                                     hipStream_t s);
+hipError_t launch_act_quant_a8_unrotated(const float *x, int m, int k, int8_t *q, float *scale,
+                                         hipStream_t s);
+hipError_t launch_q4_0_gemv_a8(const uint8_t *blocks, int rows, int cols, const int8_t *q,
+                               const float *scale, int batch, float *y, hipStream_t s);
+hipError_t launch_q4_0_gemm_a8(const uint8_t *blocks, int rows, int cols, const int8_t *q, const float *scale,
+                               int m, float *y, int num_cus, hipStream_t s);
 hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                           const int8_t *q, const float *scale, int batch, float *y,
                           int num_cus, hipStream_t s);

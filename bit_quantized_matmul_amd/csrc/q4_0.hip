@@ -18,64 +18,26 @@
 // below it plus the next 4 (2 for a final block that ends there), then
 // realigned with v_alignbyte.
 #include "bqm_common.h"
+#include "q4_0_block.h"
 
 namespace bqm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlock = 32;
-constexpr int kBlockBytes = 18;
-constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past every range: reads give 0
+constexpr int kBlock = kQ4Block;
+constexpr int kBlockBytes = kQ4BlockBytes;
 
 // Byte K of v as a float; matches v_cvt_f32_ubyteK.
 template <int K>
 __device__ __forceinline__ float ubyte_f(uint32_t v) { return (float)((v >> (8 * K)) & 0xFFu); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// One lane's block: the 16 bytes from the 4-byte-aligned address below it and
-// the next 4 (2 for a block that ends the buffer); ok == false reads zeros.
-struct BlockLoad {
-  uint4 v;
-  uint32_t v4, sh;
-};
-
-__device__ __forceinline__ BlockLoad load_block(__amdgpu_buffer_rsrc_t rw, bool ok, uint32_t off,
-                                                uint32_t total) {
-  BlockLoad L;
-  const uint32_t a4 = off & ~3u;
-  L.sh = ok ? (off & 3u) : 0u;                     // 0 or 2: blocks are 2-byte aligned
-  L.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? a4 : kOOB, 0, 0));
-  const bool w4 = ok && a4 + 20 <= total;          // the 4 bytes after exist
-  const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rw, w4 ? a4 + 16 : kOOB, 0, 0);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (ok && !w4) ? a4 + 16 : kOOB, 0, 0);
-  L.v4 = lo | hi;
-  return L;
-}
 
 // acc[b] += d * sum_{j<32} (nib_j - 8) * x[b][e0 + j] for the loaded block,
 // x from the LDS copy xs (row stride XS floats).
 template <int BATCH, int XS>
 __device__ __forceinline__ void block_dot(const BlockLoad &L, const float (*xs)[XS], int e0,
                                           float (&acc)[BATCH]) {
-  uint32_t w0, w1, w2, w3, w4;
-  if (L.sh == 0) {
-    w0 = L.v.x; w1 = L.v.y; w2 = L.v.z; w3 = L.v.w; w4 = L.v4;
-  } else {
-    w0 = __builtin_amdgcn_alignbyte(L.v.y, L.v.x, 2);
-    w1 = __builtin_amdgcn_alignbyte(L.v.z, L.v.y, 2);
-    w2 = __builtin_amdgcn_alignbyte(L.v.w, L.v.z, 2);
-    w3 = __builtin_amdgcn_alignbyte(L.v4, L.v.w, 2);
-    w4 = L.v4 >> 16;
-  }
-  const float d = half_bits_to_float((uint16_t)(w0 & 0xFFFFu));
   uint32_t nib[4];                                 // byte k of nib[w]: elements 8w+2k (low), 8w+2k+1 (high)
-  nib[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
-  nib[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
-  nib[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
-  nib[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
+  const float d = block_fields(L, nib);
 #pragma unroll
   for (int b = 0; b < BATCH; ++b) {
     float s0 = 0.0f, s1 = 0.0f;
@@ -132,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
   const int j = t % P;
   const int row = blockIdx.x * RPW + t / P;
   const bool rok = row < rows;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(blocks, total);
+  const __amdgpu_buffer_rsrc_t rw = q4_rsrc(blocks, total);
   const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
   float acc[BATCH];
 #pragma unroll

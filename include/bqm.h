@@ -96,7 +96,11 @@ int cq_analytic_levels(int bits, float *levels);
  * Sylvester-order butterfly, stages of half-width 1, 2, ..., group/2),
  * s = max|u| / 127 (1 for an all-zero row), q = clip(rint(u / s), -127, 127)
  * with correctly rounded fp32 division and half-even rounding.
- * Requires k % group == 0, group == 128, k <= 65536, x and q 16-byte aligned. */
+ * Requires k % group == 0, group == 128, k <= 65536, x and q 16-byte aligned.
+ * group == 1 is the same quantizer without the rotation (a Walsh-Hadamard
+ * transform of length 1 is the identity), for the Q4_0 products, whose
+ * weights carry none: s = max|x| / 127 over the row, q = clip(rint(x / s),
+ * -127, 127); any k <= 65536.  Other groups: BQM_ENOTSUP. */
 int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float *scale,
                       bqm_stream_t stream);
 
@@ -205,6 +209,25 @@ int q4_0_gemv(const void *blocks, int rows, int cols, const float *x, int batch,
  * when the blocks or m * cols * 4 bytes reach 2^31 (32-bit offsets). */
 int q4_0_gemm(const void *blocks, int rows, int cols, const float *x, int m, float *y,
               bqm_stream_t stream);
+
+/* Q4_0 weights against int8 activations (A8): the Q4_0 blocks of q4_0_gemv
+ * (Minueza-32M -> KMCU v1 page, sections 2-3) and the per-token codes of
+ * act_fwht_quant_a8 with group 1 (8-bit activations, Needle article,
+ * section 1).
+ *   y[t, r] = scale[t] * sum_blk fp32(d) * sum_{j<32} (nibble - 8) * q[t, 32 blk + j]
+ * Each block's sum of products is an exact int32, scaled once by the block's
+ * fp32 scale; the blocks are summed in fp32.  blocks [device] as for
+ * q4_0_gemv (16-byte aligned); q [device] int8 [batch or m, cols] (16-byte
+ * aligned base; columns >= cols meet zero weights); scale [device] fp32
+ * [batch or m]; y [device] fp32 [batch or m, rows].
+ * q4_0_gemv_a8: 1 <= batch <= 16, dot products on v_dot4_i32_i8.
+ * q4_0_gemm_a8: m >= 1, the int8 matrix cores, one block per instruction.
+ * BQM_ENOTSUP when the blocks or the codes reach 2^31 bytes (32-bit
+ * offsets), or batch > 16. */
+int q4_0_gemv_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int batch,
+                 float *y, bqm_stream_t stream);
+int q4_0_gemm_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int m,
+                 float *y, bqm_stream_t stream);
 
 /* Encode fp32 weights into a CQ blob on the device (Needle article,
  * section 1: group FWHT with the normalized Walsh-Hadamard matrix, nearest

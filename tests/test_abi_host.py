@@ -122,6 +122,18 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     # q4_0_gemv addresses its blocks with 32-bit offsets: 2^27 rows of one block is past 2^31 bytes
     assert lib.q4_0_gemv(p, 1 << 27, 32, p, 1, p, None) == E.BQM_ENOTSUP
     assert lib.q4_0_gemv(p, (1 << 27) - 1, 1, ctypes.c_void_p(4100), 1, p, None) == E.BQM_ENOTSUP
+    # A8 without the rotation: group 1 takes any k; other groups are not built
+    assert lib.act_fwht_quant_a8(p, 1, 312, 2, p, p, None) == E.BQM_ENOTSUP
+    assert lib.act_fwht_quant_a8(p, 1, 312, 3, p, p, None) == E.BQM_EINVAL
+    assert lib.act_fwht_quant_a8(p, 1, 65537, 1, p, p, None) == E.BQM_ENOTSUP
+    assert lib.act_fwht_quant_a8(ctypes.c_void_p(4100), 1, 312, 1, p, p, None) == E.BQM_EALIGN
+    for fn in (lib.q4_0_gemv_a8, lib.q4_0_gemm_a8):
+        assert fn(None, 4, 312, p, p, 1, p, None) == E.BQM_EINVAL
+        assert fn(p, 4, 312, p, p, 0, p, None) == E.BQM_EINVAL
+        assert fn(p, 4, 312, ctypes.c_void_p(4100), p, 1, p, None) == E.BQM_EALIGN
+        assert fn(p, 1 << 27, 32, p, p, 1, p, None) == E.BQM_ENOTSUP          # blocks past 2^31 bytes
+    assert lib.q4_0_gemv_a8(p, 4, 312, p, p, 17, p, None) == E.BQM_ENOTSUP
+    assert lib.q4_0_gemm_a8(p, 4, 1 << 20, p, p, 4096, p, None) == E.BQM_ENOTSUP   # codes past 2^31 bytes
     assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL
     assert lib.q4_0_pack(p, 0, 312, p, None) == E.BQM_EINVAL
     assert lib.cq_codebook_fit(p, 1 << 20, 16, 200, None, p, None) == E.BQM_ENOTSUP
