@@ -19,7 +19,7 @@ bit-width sweep, the same decode layer shapes at 4 and
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|sweep|batched|kmcu|floor|copy|c1
+       python bench.py --only dominant|decode|prefill|q4_0|q4_0_prefill|q4_0_a8|sweep|batched|kmcu|floor|copy|c1
        (profiling runs)
 """
 from __future__ import annotations
@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["dominant", "decode", "prefill", "q4_0", "q4_0_prefill", "sweep",
-                                       "batched", "kmcu", "floor", "copy", "c1"])
+                                       "batched", "kmcu", "floor", "copy", "c1", "q4_0_a8"])
     ap.add_argument("--no-graph", action="store_true",
                     help="launch kernel-mean sequences eagerly (for counter collection)")
     return ap.parse_args()
@@ -503,6 +503,56 @@ def bench_q4_0_prefill(B, torch, dev, steps, warmup, m=512):
                 head_frac=head_tf / FP32_MFMA_PEAK_TFLOPS)
 
 
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix, published
+
+
+def bench_q4_0_a8(B, torch, dev, steps, warmup, m=512):
+    """The Minueza Q4_0 pass with int8 activations (A8, no rotation): decode
+    (one token) and prefill (m tokens), graph-timed; each matrix's input is
+    quantized with act_fwht_quant_a8 (group 1) then multiplied.  Times with
+    the A8 launches and for the products alone are both given."""
+    from bit_quantized_matmul_amd import inputs
+    wl = inputs.minueza_q4_0_pass()
+    rng = inputs.rng_for(13)
+    dec, pre, total, flops = [], [], 0, 0
+    for (label, w), x in zip(wl.weights, wl.acts):
+        rows, cols = w.shape
+        blocks = B.q4_0_pack(torch.from_numpy(w).to(dev))
+        total += blocks.numel()
+        xd = torch.from_numpy(x).to(dev)
+        q1, s1 = B.act_fwht_quant_a8(xd, group=1)
+        dec.append((rows, cols, blocks, xd, q1, s1, torch.empty((1, rows), dtype=torch.float32, device=dev)))
+        xp = torch.from_numpy(inputs.activations(rng, m, cols)).to(dev)
+        qp, sp = B.act_fwht_quant_a8(xp, group=1)
+        pre.append((rows, cols, blocks, xp, qp, sp, torch.empty((m, rows), dtype=torch.float32, device=dev)))
+        flops += 2 * m * rows * cols
+    torch.cuda.synchronize()
+
+    def one(items, gemm, with_a8):
+        def run():
+            for rows, cols, blocks, x, q, s, y in items:
+                if with_a8:
+                    B.act_fwht_quant_a8(x, group=1, q=q, scale=s)
+                (B.q4_0_gemm_a8 if gemm else B.q4_0_gemv_a8)(blocks, rows, cols, q, s, y=y)
+        return run
+
+    def t(fn):
+        return sorted(graph_repeats_ms(torch, [fn] * max(steps, 5), repeats=5))[2]
+
+    d_a8, d_prod = t(one(dec, False, True)), t(one(dec, False, False))
+    p_a8, p_prod = t(one(pre, True, True)), t(one(pre, True, False))
+    rows, cols, blocks, x, q, s, y = pre[-1]
+    head = sorted(graph_repeats_ms(torch, [lambda: B.q4_0_gemm_a8(blocks, rows, cols, q, s, y=y)] * 8))[2]
+    head_tops = 2 * m * rows * cols / head / 1e9
+    return dict(
+        decode=dict(launches=2 * len(dec), bytes=total, us_with_a8=d_a8 * 1e3, us_products_only=d_prod * 1e3,
+                    gbps_products_only=total / d_prod / 1e6, note="weights warm in the Infinity Cache"),
+        prefill=dict(tokens=m, gop=flops / 1e9, us_with_a8=p_a8 * 1e3, us_products_only=p_prod * 1e3,
+                     tops_products_only=flops / p_prod / 1e9,
+                     frac_int8_peak=flops / p_prod / 1e9 / INT8_MFMA_PEAK_TOPS,
+                     head_us=head * 1e3, head_tops=head_tops, head_frac_int8_peak=head_tops / INT8_MFMA_PEAK_TOPS))
+
+
 PCIE_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
@@ -777,6 +827,9 @@ def main():
     if args.only == "q4_0_prefill":
         print(json.dumps(bench_q4_0_prefill(B, torch, dev, args.steps, args.warmup)))
         return
+    if args.only == "q4_0_a8":
+        print(json.dumps(bench_q4_0_a8(B, torch, dev, args.steps, args.warmup)))
+        return
     if args.only == "sweep":
         print(json.dumps(bench_sweep(B, torch, dev, cbs, args.steps)))
         return
@@ -802,6 +855,9 @@ def main():
     log(f"q4_0 pass {q4['us_graph']:.1f} us (graph)")
     q4p = bench_q4_0_prefill(B, torch, dev, args.steps, args.warmup)
     log(f"q4_0 prefill pass, {q4p['tokens']} tokens: {q4p['us_graph']:.1f} us, {q4p['tflops']:.1f} TFLOP/s")
+    qa8 = bench_q4_0_a8(B, torch, dev, args.steps, args.warmup)
+    log(f"q4_0 A8: decode pass {qa8['decode']['us_with_a8']:.1f} us with A8 ({qa8['decode']['us_products_only']:.1f} "
+        f"products only); prefill {qa8['prefill']['us_with_a8']:.1f} us ({qa8['prefill']['tops_products_only']:.1f} TOP/s)")
     sweep = bench_sweep(B, torch, dev, cbs, args.steps)
     log("sweep done")
     bat = bench_batched(B, torch, dev, cbs, args.steps)
@@ -864,6 +920,7 @@ def main():
         "prefill_gemm": pre,
         "q4_0_minueza_pass": q4,
         "q4_0_minueza_prefill_512": q4p,
+        "q4_0_a8_minueza": qa8,
         "bit_sweep_14336x4096": sweep,
         "batched_decode_cb4": bat,
         "kmcu_load_minueza_tied": km,
