@@ -634,6 +634,12 @@ def bench_sweep(B, torch, dev, cbs, steps):
                 for k in range(n)])
             out[f"{names[code]}_b{batch}"] = dict(us=d * 1e3, gbps=nb / d / 1e6,
                                                   frac=nb / d / 1e6 / HBM_PEAK_GBPS)
+            if code in (1, 5):                   # the lookup-table kernel on the same weights
+                d = graph_mean_ms(torch, [
+                    (lambda k=k: B.cq_gemv_lut(pool[k], lay, q, s, y=y))
+                    for k in range(n)])
+                out[f"{names[code]}_lut_b{batch}"] = dict(us=d * 1e3, gbps=nb / d / 1e6,
+                                                          frac=nb / d / 1e6 / HBM_PEAK_GBPS)
         del pool, blob
         torch.cuda.synchronize()
     return out

@@ -23,7 +23,7 @@ EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
     "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
     "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data", "cq_gemv_f32_noalloc",
-    "q4_0_gemv_a8", "q4_0_gemm_a8",
+    "q4_0_gemv_a8", "q4_0_gemm_a8", "cq_gemv_lut",
 )
 KMCU_F32, KMCU_Q4 = 1, 2
 
@@ -92,6 +92,7 @@ def load_library() -> ctypes.CDLL:
         "cq_gemv": ([P, LP, F, P, P, I, P, P], I),
         "cq_gemv_f32": ([P, LP, F, P, I, P, P, P, P], I),
         "cq_gemv_f32_noalloc": ([P, LP, F, P, I, P, P], I),
+        "cq_gemv_lut": ([P, LP, P, P, I, P, P], I),
         "cq_gemm": ([P, LP, F, P, P, I, P, P], I),
         "q4_0_gemv": ([P, I, I, P, I, P, P], I),
         "q4_0_gemm": ([P, I, I, P, I, P, P], I),
@@ -228,6 +229,22 @@ def cq_gemv(blob, layout: CqLayout, codebook, q, scale, y=None):
     cb, _keep = _codebook_ptr(codebook, layout.levels)
     _check("cq_gemv", load_library().cq_gemv(
         _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), cb, _dev(q, torch.int8, "q"),
+        _dev(scale, torch.float32, "scale"), batch, _dev(y, torch.float32, "y"), _stream()))
+    return y
+
+
+def cq_gemv_lut(blob, layout: CqLayout, q, scale, y=None):
+    """Binary / ternary CQ [rows, cols] x int8 q [batch, cols] -> fp32 y [batch, rows],
+    the lookup-table kernel."""
+    torch = _torch()
+    batch = _rows2d(q, layout.cols, "q")
+    _at_least(blob, layout.total_bytes, "blob")
+    _shape(scale, (batch,), "scale")
+    if y is None:
+        y = torch.empty((batch, layout.rows), dtype=torch.float32, device=q.device)
+    _shape(y, (batch, layout.rows), "y")
+    _check("cq_gemv_lut", load_library().cq_gemv_lut(
+        _dev(blob, torch.uint8, "blob"), ctypes.byref(layout), _dev(q, torch.int8, "q"),
         _dev(scale, torch.float32, "scale"), batch, _dev(y, torch.float32, "y"), _stream()))
     return y
 

@@ -295,6 +295,23 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
                                       scale_out, cus, (hipStream_t)stream));
 }
 
+int cq_gemv_lut(const void *blob, const bqm_cq_layout *layout, const int8_t *q, const float *scale, int batch,
+                float *y, bqm_stream_t stream) {
+  if (!blob || !q || !scale || !y || batch < 1) return BQM_EINVAL;
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  if (!cq_gemv_lut_supported(*layout, batch)) return BQM_ENOTSUP;
+  LevelTable T;
+  rc = make_table(layout->bits, nullptr, &T);
+  if (rc) return rc;
+  if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u)) return BQM_EALIGN;
+  int cus;
+  rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_cq_gemv_lut((const uint8_t *)blob, *layout, T, q, scale, batch, y, cus,
+                                      (hipStream_t)stream));
+}
+
 int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const float *codebook,
                         const float *x, int batch, float *y, bqm_stream_t stream) {
   if (!blob || !x || !y || batch < 1) return BQM_EINVAL;

@@ -125,6 +125,9 @@ bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch);
 hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                              const int8_t *q, const float *scale, int batch, float *y, int num_cus,
                              hipStream_t s);
+bool cq_gemv_lut_supported(const bqm_cq_layout &L, int batch);
+hipError_t launch_cq_gemv_lut(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T, const int8_t *q,
+                              const float *scale, int batch, float *y, int num_cus, hipStream_t s);
 hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                               const int8_t *q, const float *scale, int batch, float *y,
                               int num_cus, hipStream_t s);

@@ -149,6 +149,23 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
                 const float *x, int batch, float *y, int8_t *q_out, float *scale_out,
                 bqm_stream_t stream);
 
+/* Lookup-table decode GEMV for the binary and ternary sets (bits 1 and 5):
+ * the cq_gemv sum computed the Four-Russians / T-MAC way ("llama.cpp on a TV
+ * box and a 2013 iPad Air", the kernel table's 1-bit LUT entry).  Each
+ * workgroup builds, in LDS, a 16-entry table of int16 partial sums per 4
+ * activations (binary: every sign pattern of 4 bits) or per 2 activations
+ * (ternary: every pair of 2-bit fields), the tokens side by side in an entry;
+ * each nibble of the index stream then costs one table read.  Sums are exact
+ * integers per 32-index chunk, scaled by the fp32 group norm and added in
+ * fp32.  blob [device] bits 1 or 5 (BQM_ENOTSUP for other codes), group 128;
+ * q [device] int8 [batch, cols] (act_fwht_quant_a8); scale [device] fp32
+ * [batch]; y [device] fp32 [batch, rows].  1 <= batch <= 16 (launches of up
+ * to 4 tokens, fewer where their tables would pass 128 KB of LDS: 16 cols
+ * bytes a token for ternary, 8 cols for binary); cols <= 8192, BQM_ENOTSUP
+ * otherwise. */
+int cq_gemv_lut(const void *blob, const bqm_cq_layout *layout, const int8_t *q, const float *scale, int batch,
+                float *y, bqm_stream_t stream);
+
 /* cq_gemv_f32 for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Computes exactly what cq_gemv_f32 computes with q_out and scale_out given

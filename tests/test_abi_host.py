@@ -134,6 +134,14 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
         assert fn(p, 1 << 27, 32, p, p, 1, p, None) == E.BQM_ENOTSUP          # blocks past 2^31 bytes
     assert lib.q4_0_gemv_a8(p, 4, 312, p, p, 17, p, None) == E.BQM_ENOTSUP
     assert lib.q4_0_gemm_a8(p, 4, 1 << 20, p, p, 4096, p, None) == E.BQM_ENOTSUP   # codes past 2^31 bytes
+    # the lookup-table GEMV: binary and ternary only, widths its LDS tables hold
+    assert lib.cq_gemv_lut(p, ctypes.byref(lay), p, p, 1, p, None) == E.BQM_ENOTSUP       # 4-bit
+    b1 = binding.cq_pack_info(64, 8192, 128, 1)
+    assert lib.cq_gemv_lut(p, ctypes.byref(b1), p, p, 0, p, None) == E.BQM_EINVAL
+    assert lib.cq_gemv_lut(p, ctypes.byref(b1), p, p, 17, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_lut(p, ctypes.byref(binding.cq_pack_info(64, 8320, 128, 1)), p, p, 1, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_lut(p, ctypes.byref(binding.cq_pack_info(64, 8320, 128, 5)), p, p, 1, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_lut(ctypes.c_void_p(4100), ctypes.byref(b1), p, p, 1, p, None) == E.BQM_EALIGN
     assert lib.cq_pack(p, ctypes.byref(bad), cb, p, None, None) == E.BQM_EINVAL
     assert lib.q4_0_pack(p, 0, 312, p, None) == E.BQM_EINVAL
     assert lib.cq_codebook_fit(p, 1 << 20, 16, 200, None, p, None) == E.BQM_ENOTSUP

@@ -609,3 +609,31 @@ def test_gemm_tiny_norm_rows_stay_within_bound(codebooks):
     y = host(B.cq_gemm(dev(ocq.make_blob(idx, n16, 128, 4)), lay, lv, dev(q), dev(s)))
     st = P.check_cq(y, idx, n16, 128, 4, lv, q, s, P.TOL_FOLD, "gemm tiny-norm rows")
     assert st["worst_row_rel"] < 2e-3
+
+
+# ---------------------------------------------- the lookup-table GEMV (T-MAC)
+
+# 1..4 tokens in one launch (4 side by side, 3 with a zero fourth), 5 and 16
+# in several; widths up to its 8192 limit, where the ternary tables of two
+# tokens no longer fit and the launches take fewer; rows shorter than a wave
+# of chunks (128, 384) and several chunks a lane (8192)
+@pytest.mark.parametrize("code", [1, 5])
+@pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (130, 4096, 2), (77, 4096, 3),
+                                             (64, 4096, 4), (33, 8192, 1), (33, 8192, 4), (5, 128, 2),
+                                             (1000, 384, 5), (1, 256, 1), (40, 1024, 16)])
+def test_cq_gemv_lut_parity(code, rows, cols, batch, codebooks):
+    rng = np.random.default_rng(1700 + code * 3 + rows + cols + batch)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, batch, codebooks)
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    y = host(B.cq_gemv_lut(dev(blob), lay, dev(q), dev(s)))
+    P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"cq_gemv_lut code {code} {rows}x{cols} b{batch}")
+
+
+@pytest.mark.parametrize("code", [1, 5])
+def test_cq_gemv_lut_mixed_scale_rows(code, codebooks):
+    rng = np.random.default_rng(1750 + code)
+    x, lv, idx, n16, blob = mixed_case(rng, 60, 4096, code, 3, codebooks)
+    q, s = oa8.act_quant_a8(x, 128, "fp32")
+    y = host(B.cq_gemv_lut(dev(blob), B.cq_pack_info(60, 4096, 128, code), dev(q), dev(s)))
+    assert np.all(y[:, 30] == 0.0)
+    P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"mixed cq_gemv_lut code {code}")
