@@ -228,29 +228,33 @@ struct GemvArgs {
 };
 
 // q = clip(rint(u / s), -127, 127) with u / s correctly rounded, computed as
-// rint(u * inv) unless u * inv lies within 1e-4 of a half-integer: for
-// |u / s| <= 127 the product differs from the correctly rounded quotient by at
-// most 2.3e-5, so away from the rounding boundaries both give the same
-// integer.  Near a boundary (rare) the quotient is taken exactly.  (The clip
-// binds only when amax / 127 underflows to zero.)
+// rint(u * inv), inv = rcp(s) (within 1 ulp of 1 / s), unless u * inv lies
+// within 1e-4 of a half-integer: for |u / s| <= 127 the product differs from
+// the correctly rounded quotient by at most 2.3e-5, so away from the rounding
+// boundaries both give the same integer.  Near a boundary (rare) the quotient
+// is taken exactly.  The distance test is one maximum over the lanes'
+// elements.  The clip binds only when s is subnormal (for a normal
+// s = RN(amax / 127), |u| / s <= 127 (1 + 2^-23) rounds to at most 127), so it
+// runs only then (`clip`, uniform).
 template <int N>
-__device__ __forceinline__ void a8_codes(const float (&u)[N], float s, float inv, float (&code)[N]) {
-  bool near = false;
+__device__ __forceinline__ void a8_codes(const float (&u)[N], float s, float inv, bool clip,
+                                         float (&code)[N]) {
+  float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float yv = u[i] * inv;
-    code[i] = rintf(yv);
-    near |= fabsf(yv - code[i]) > 0.4999f;
+    code[i] = rintf(u[i] * inv);
+    dmax = fmaxf(dmax, fabsf(fmaf(u[i], inv, -code[i])));
   }
-  if (near) {
+  if (dmax > 0.4999f) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const float yv = u[i] * inv;
-      if (fabsf(yv - code[i]) > 0.4999f) code[i] = rintf(__fdiv_rn(u[i], s));
+      if (fabsf(fmaf(u[i], inv, -code[i])) > 0.4999f) code[i] = rintf(__fdiv_rn(u[i], s));
     }
   }
+  if (clip) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) code[i] = __builtin_amdgcn_fmed3f(code[i], -127.0f, 127.0f);
+    for (int i = 0; i < N; ++i) code[i] = __builtin_amdgcn_fmed3f(code[i], -127.0f, 127.0f);
+  }
 }
 
 // DPP quad permutations: lane i reads lane i^1 / i^2 of its group of four.
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
   const int rows = A.rows, cols = A.cols;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: the row math is scalar
   const int S = A.S;                                // waves per row (divides kWaves)
   const int P = FULL ? kWave : (1 << A.plog2);
   const int rpw = FULL ? 1 : (kWave >> A.plog2);
@@ -356,13 +360,35 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
 #pragma unroll
   for (int i = 0; i < 16; ++i) lv_lane = (lane == i) ? (int)T.h16[i] : lv_lane;
 
-  // work item (k, part) -> ring slot; items past the wave's end read zeros
+  // work item (k, part) -> ring slot; items past the wave's end read zeros.
+  // FULL: the wave's row of an item is read through descriptors whose range
+  // is that row (empty for items past the wave's end), so chunks past the
+  // row's end read zeros without traffic and the per-lane offsets are fixed;
+  // the norm descriptor starts at the 4-byte boundary at or below the row's
+  // first norm and a lane's (unaligned) dword starts at its group's norm, so
+  // the norm is the low half.
   const uint32_t lane_idx = (uint32_t)(rs * row_bytes + li * kCB);
   const uint32_t lane_nrm = (uint32_t)(li >> 2) * 2u;                 // FULL: rs == 0
   auto issue = [&](int k, int part, Chunk<IB> (&dst)[CPL], uint32_t (&ndst)[CPL]) {
     const int rbase = r0 + gw * rpw + k * rows_per_iter;         // row of this lane: rbase + rs
     const bool live = (k < iters) && (rbase + rs < r1);
     const int sbase = (si * nparts + part) * CPL;                // first slot of the item
+    if constexpr (FULL) {
+      const uint32_t nrow = (uint32_t)rbase * (uint32_t)ng;       // the row's first norm
+      const uint32_t adj = (nrow & 1u) * 2u;
+      const __amdgpu_buffer_rsrc_t ri =
+          make_rsrc(A.idx + (size_t)rbase * row_bytes, live ? (uint32_t)row_bytes : 0u);
+      const __amdgpu_buffer_rsrc_t rn =
+          make_rsrc(A.norms + (nrow & ~1u), live ? (uint32_t)(2 * ng + 2) + adj : 0u);
+      const uint32_t oi = lane_idx + (uint32_t)(sbase * P * kCB);
+      const uint32_t on = lane_nrm + adj + (uint32_t)(sbase * (P / 2));
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) {
+        dst[m] = load_chunk<IB>(ri, oi + (uint32_t)(m * P * kCB));
+        ndst[m] = __builtin_amdgcn_raw_buffer_load_b32(rn, on + (uint32_t)(m * (P / 2)), 0, 0);
+      }
+      return;
+    }
     uint32_t vi = (uint32_t)rbase * (uint32_t)row_bytes + lane_idx + (uint32_t)(sbase * P * kCB);
     // norm of chunk c = li + P * slot is that of group c / 4; with P = 64 the
     // group of slot m is the group of slot 0 plus 16 m (short row slots have
@@ -421,8 +447,6 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) sclw[b] = __builtin_amdgcn_raw_buffer_load_b32(rscl, 4 * b, 0, 0);
   }
-  issue(ik, ipart, ring[0], nring[0]);
-  advance(ik, ipart);
   // the replicated level table: a wave instruction writes four rows (16 lanes
   // x 16 bytes each); a lane takes the levels its row needs from lanes 0..15
   // with ds_bpermute
@@ -442,6 +466,10 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
         *reinterpret_cast<uint4 *>(tab + (4 * u + (lane >> 4)) * 256 + (lane & 15) * 16) = ent[i];
     }
   }
+  // the first item goes out only now, so that the activations (every wave's
+  // first loads) are not queued behind weight loads of other waves
+  issue(ik, ipart, ring[0], nring[0]);
+  advance(ik, ipart);
   // vmcnt(2 CPL): everything but the first item's loads has landed
   __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPL));
 
@@ -487,7 +515,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < kSeg; ++i) m = fmaxf(m, fabsf(v[i]));
-      const int bj = (t + j * kThreads) / spr;
+      const int bj = BATCH == 1 ? 0 : (t + j * kThreads) / spr;
 #pragma unroll
       for (int b = 0; b < BATCH; ++b)
         if (bj == b) lmax[b] = fmaxf(lmax[b], m);
@@ -505,14 +533,14 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       float mx = amax_red[b * kWaves];
       for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, amax_red[b * kWaves + w]);
       scs[b] = (mx > 0.0f) ? __fdiv_rn(mx, 127.0f) : 1.0f;
-      invs[b] = 1.0f / scs[b];
+      invs[b] = __builtin_amdgcn_rcpf(scs[b]);
     }
     if (t < BATCH) s_blk[t] = scs[t];
 #pragma unroll
     for (int j = 0; j < SEGS; ++j) {
       const int sg = t + j * kThreads;
       if (sg < nseg) {
-        const int b = sg / spr, k0 = (sg - b * spr) * kSeg;
+        const int b = BATCH == 1 ? 0 : sg / spr, k0 = (sg - b * spr) * kSeg;
         const int c = k0 >> 5, i0 = (k0 & 31) >> 3;     // chunk, and its first quarter (0 or 2)
         float sc = scs[0], inv = invs[0];
 #pragma unroll
@@ -525,7 +553,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
           float ub[8], cb[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ub[i] = xv[j][8 * k8 + i];
-          a8_codes<8>(ub, sc, inv, cb);
+          a8_codes<8>(ub, sc, inv, sc < 1.17549435e-38f, cb);
 #pragma unroll
           for (int p = 0; p < 4; ++p)
             pr[4 * k8 + p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cb[2 * p], cb[2 * p + 1]));
@@ -572,6 +600,10 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       for (int m = 0; m < CPL; ++m) {
         const int c = li + P * (si * CPL + m);
         qpairs(b, c < C ? c : 0, qreg[b][m]);
+        // chunks past the row's end: zero activations, so their (zero-index)
+        // lookups add nothing whatever the norm
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qreg[b][m][j] = c < C ? qreg[b][m][j] : 0u;
       }
   }
 
@@ -585,7 +617,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
     const int sbase = (si * nparts + ppart) * CPL;
     // which half of the norm word: parity of the chunk's group index (for P = 64
     // the same for all CPL chunks: their groups differ by multiples of 16)
-    const uint32_t nsh = (uint32_t)((row * ng + ((li + P * sbase) >> 2)) & 1) * 16u;
+    const uint32_t nsh = FULL ? 0u : (uint32_t)((row * ng + ((li + P * sbase) >> 2)) & 1) * 16u;
     // software pipeline over the item's chunks: the lookups of chunk m+1 are
     // in flight while chunk m's dot products run; sched_barrier keeps the
     // compiler from hoisting further (which would blow the register budget)
@@ -598,7 +630,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       for (int j = 0; j < 16; ++j) W[j] = Wn[j];
       if (m + 1 < CPL) lookup<IB>(cur[m + 1], tab, laneoff, Wn);
       const int c = li + P * (sbase + m);
-      const bool cok = c < C;
+      const bool cok = (FULL && QREG) || c < C;       // QREG: zero activations past the row
       const float nv = cok ? half_bits_to_float((uint16_t)(ncur[m] >> nsh)) : 0.0f;
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
