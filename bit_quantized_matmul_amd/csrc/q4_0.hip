@@ -31,6 +31,13 @@ constexpr int kBlockBytes = kQ4BlockBytes;
 template <int K>
 __device__ __forceinline__ float ubyte_f(uint32_t v) { return (float)((v >> (8 * K)) & 0xFFu); }
 
+// Rotation by R lanes inside each 16-lane DPP row (row_ror:R).
+template <int R>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + R,
+                                                                 0xF, 0xF, false));
+}
+
 // acc[b] += d * sum_{j<32} (nib_j - 8) * x[b][e0 + j] for the loaded block,
 // x from the LDS copy xs (row stride XS floats).
 template <int BATCH, int XS>
@@ -121,6 +128,104 @@ __global__ __launch_bounds__(kThreads) void q4_0_gemv_kernel(
   }
 }
 
+// Rows of 9 to 16 blocks: 16 lanes (one DPP row) per matrix row, one block
+// each, and the workgroup walks NT row tiles (tiles blockIdx.x + i *
+// gridDim.x).  A lane's 32 activations (those of its block column, zero past
+// cols) come straight from global memory into registers, ahead of the NT
+// tiles' block loads, so there is no LDS staging and no barrier: each tile is
+// summed as soon as its loads land.  The row sum closes with the rotations
+// by 1, 2, 4, 8 inside the 16-lane row (every lane ends with the total, in
+// the same fixed order).  VEC: cols % 4 == 0 and x 16-byte aligned.
+typedef uint32_t u32x4q __attribute__((ext_vector_type(4)));
+template <int BATCH, int NT, bool VEC>
+__global__ __launch_bounds__(kThreads) void q4_0_gemv_rows_kernel(
+    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t total,
+    const float *__restrict__ x, float *__restrict__ y) {
+  constexpr int P = 16;
+  constexpr int RPW = kThreads / P;        // rows per tile
+  const int t = threadIdx.x;
+  const int j = t % P;
+  const __amdgpu_buffer_rsrc_t rw = q4_rsrc(blocks, total);
+  const __amdgpu_buffer_rsrc_t rx = q4_rsrc(x, (uint32_t)((size_t)BATCH * cols * 4));
+  // activations of block column j: 8 loads of 4 floats per token (columns
+  // past cols read 0: each token's range is checked through its own offset)
+  float xr[BATCH][kBlock];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+    for (int u = 0; u < kBlock / 4; ++u) {
+      const int c = j * kBlock + 4 * u;
+      if constexpr (VEC) {
+        const u32x4q v = __builtin_bit_cast(u32x4q, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rx, c < cols ? (uint32_t)((b * cols + c) * 4) : kQ4OOB, 0, 0));
+        xr[b][4 * u + 0] = __uint_as_float(v.x);
+        xr[b][4 * u + 1] = __uint_as_float(v.y);
+        xr[b][4 * u + 2] = __uint_as_float(v.z);
+        xr[b][4 * u + 3] = __uint_as_float(v.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          xr[b][4 * u + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rx, c + e < cols ? (uint32_t)((b * cols + c + e) * 4) : kQ4OOB, 0, 0));
+      }
+    }
+  BlockLoad L[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int row = (blockIdx.x + i * gridDim.x) * RPW + t / P;
+    const bool ok = row < rows && j < nblk;
+    L[i] = load_block(rw, ok, ok ? (uint32_t)(((size_t)row * nblk + j) * kBlockBytes) : 0u, total);
+  }
+  // sum_j (nib_j - 8) x_j = sum_j nib_j x_j - 8 sum_j x_j: the lane's
+  // activations are the same for every tile, so their sum is taken once
+  // (nib_j x_j is exact; the two sums round like any fp32 reduction)
+  float xs8[BATCH];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kBlock; e += 2) {
+      a0 += xr[b][e];
+      a1 += xr[b][e + 1];
+    }
+    xs8[b] = 8.0f * (a0 + a1);
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int row = (blockIdx.x + i * gridDim.x) * RPW + t / P;
+    uint32_t nib[4];
+    const float d = block_fields(L[i], nib);
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = nib[w] & 0x0F0F0F0Fu;
+        const uint32_t hi = (nib[w] >> 4) & 0x0F0F0F0Fu;
+        s0 = fmaf(ubyte_f<0>(lo), xr[b][8 * w + 0], s0);
+        s1 = fmaf(ubyte_f<0>(hi), xr[b][8 * w + 1], s1);
+        s0 = fmaf(ubyte_f<1>(lo), xr[b][8 * w + 2], s0);
+        s1 = fmaf(ubyte_f<1>(hi), xr[b][8 * w + 3], s1);
+        s0 = fmaf(ubyte_f<2>(lo), xr[b][8 * w + 4], s0);
+        s1 = fmaf(ubyte_f<2>(hi), xr[b][8 * w + 5], s1);
+        s0 = fmaf(ubyte_f<3>(lo), xr[b][8 * w + 6], s0);
+        s1 = fmaf(ubyte_f<3>(hi), xr[b][8 * w + 7], s1);
+      }
+      float v = d * ((s0 + s1) - xs8[b]);
+      v += row_ror<1>(v);
+      v += row_ror<2>(v);
+      v += row_ror<4>(v);
+      v += row_ror<8>(v);
+      acc[b] = v;
+    }
+    if (row < rows && j == 0) {
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) y[(size_t)b * rows + row] = acc[b];
+    }
+  }
+}
+
 // One thread per block.  fp32 throughout, matching the page's numpy:
 // amax = max|w|; d = amax / 8 (1 if amax == 0); q = clip(rint(w / d), -8, 7).
 __global__ __launch_bounds__(kThreads) void q4_0_pack_kernel(const float *__restrict__ w, int rows,
@@ -156,12 +261,36 @@ __global__ __launch_bounds__(kThreads) void q4_0_pack_kernel(const float *__rest
   }
 }
 
+constexpr int kRowsWgPerCu = 2;            // row-tile kernel: workgroups per CU
+constexpr int kRowsMaxNT = 8;              // ... and at most this many tiles a workgroup
+
+template <int BATCH, bool VEC>
+hipError_t launch_rows(const uint8_t *blocks, int rows, int cols, int nblk, uint32_t total,
+                       const float *x, float *y, int num_cus, hipStream_t s) {
+  const int tiles = (rows + kThreads / 16 - 1) / (kThreads / 16);
+  int grid = num_cus * kRowsWgPerCu;
+  if (grid * kRowsMaxNT < tiles) grid = (tiles + kRowsMaxNT - 1) / kRowsMaxNT;
+  if (grid > tiles) grid = tiles;
+  const int nt = (tiles + grid - 1) / grid;
+  if (nt <= 1) q4_0_gemv_rows_kernel<BATCH, 1, VEC><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y);
+  else if (nt <= 2) q4_0_gemv_rows_kernel<BATCH, 2, VEC><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y);
+  else if (nt <= 4) q4_0_gemv_rows_kernel<BATCH, 4, VEC><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y);
+  else q4_0_gemv_rows_kernel<BATCH, 8, VEC><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y);
+  return hipGetLastError();
+}
+
 template <int BATCH>
 hipError_t launch_batch(const uint8_t *blocks, int rows, int cols, int nblk, uint32_t total,
-                        const float *x, float *y, hipStream_t s) {
+                        const float *x, float *y, int num_cus, hipStream_t s) {
   // lanes per row: the power of two covering the row's blocks (4 .. 64)
   int P = 4;
   while (P < 64 && P < nblk) P *= 2;
+  // tall matrices of 9 to 16 blocks a row: persistent row tiles
+  if (P == 16 && rows >= num_cus * (kThreads / 16) * 2) {
+    const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    return vec ? launch_rows<BATCH, true>(blocks, rows, cols, nblk, total, x, y, num_cus, s)
+               : launch_rows<BATCH, false>(blocks, rows, cols, nblk, total, x, y, num_cus, s);
+  }
   const int grid = (rows + kThreads / P - 1) / (kThreads / P);
   switch (P) {
     case 4: q4_0_gemv_kernel<BATCH, 4><<<grid, kThreads, 0, s>>>(blocks, rows, cols, nblk, total, x, y); break;
@@ -177,7 +306,6 @@ hipError_t launch_batch(const uint8_t *blocks, int rows, int cols, int nblk, uin
 
 hipError_t launch_q4_0_gemv(const uint8_t *blocks, int rows, int cols, const float *x, int batch,
                             float *y, int num_cus, hipStream_t s) {
-  (void)num_cus;
   const int nblk = (cols + kBlock - 1) / kBlock;
   const size_t total = (size_t)rows * nblk * kBlockBytes;
   if (total >= ((size_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit buffer offsets
@@ -186,9 +314,9 @@ hipError_t launch_q4_0_gemv(const uint8_t *blocks, int rows, int cols, const flo
     const float *xb = x + (size_t)b0 * cols;
     float *yb = y + (size_t)b0 * rows;
     hipError_t e;
-    if (nb == 4) e = launch_batch<4>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
-    else if (nb == 2) e = launch_batch<2>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
-    else e = launch_batch<1>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, s);
+    if (nb == 4) e = launch_batch<4>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, num_cus, s);
+    else if (nb == 2) e = launch_batch<2>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, num_cus, s);
+    else e = launch_batch<1>(blocks, rows, cols, nblk, (uint32_t)total, xb, yb, num_cus, s);
     if (e != hipSuccess) return e;
     b0 += nb;
   }

@@ -271,6 +271,21 @@ def test_q4_0_gemv_parity(rows, cols, batch):
     P.check_q4_0(y, blk, cols, x, label=f"q4_0_gemv {rows}x{cols} b{batch}")
 
 
+# tall matrices of 9..16 blocks a row take the persistent row-tile kernel
+# (16 lanes a row, activations in registers): a full last block ending the
+# buffer (512 cols), ragged ones with cols % 4 != 0 (301, 318: 4-byte
+# activation loads), and batches split 4+1, 2+1 and 4+2
+@pytest.mark.parametrize("rows,cols,batch", [(8192, 512, 1), (9001, 301, 3), (32002, 312, 5),
+                                             (8200, 318, 6)])
+def test_q4_0_gemv_row_tiles(rows, cols, batch):
+    rng = np.random.default_rng(610 + rows + cols + batch)
+    w = inputs.weight_matrix(rng, rows, cols)
+    x = inputs.activations(rng, batch, cols)
+    blk = oq4.encode(w)
+    y = host(B.q4_0_gemv(dev(blk.ravel()), rows, cols, dev(x)))
+    P.check_q4_0(y, blk, cols, x, label=f"q4_0_gemv rows {rows}x{cols} b{batch}")
+
+
 # the Minueza layer and head shapes at a prompt's worth of tokens, a ragged
 # token count, cols past a whole block (1092) and not a multiple of 4 (33, 101:
 # the 4-byte activation loads), single rows, tokens and columns
