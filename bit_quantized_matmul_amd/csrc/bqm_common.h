@@ -122,6 +122,10 @@ bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch);
 // Base-3 packed ternary (bits code 6): one token with up to 128 groups a row,
 // or 2..16 tokens (launches of up to 4) with up to 64.
 bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch);
+bool cq_t3_mma_supported(const bqm_cq_layout &L, int batch);
+hipError_t launch_cq_t3_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                            const int8_t *q, const float *scale, int batch, float *y, int num_cus,
+                            hipStream_t s);
 hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                              const int8_t *q, const float *scale, int batch, float *y, int num_cus,
                              hipStream_t s);

@@ -364,9 +364,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
   // FULL: the wave's row of an item is read through descriptors whose range
   // is that row (empty for items past the wave's end), so chunks past the
   // row's end read zeros without traffic and the per-lane offsets are fixed;
-  // the norm descriptor starts at the 4-byte boundary at or below the row's
-  // first norm and a lane's (unaligned) dword starts at its group's norm, so
-  // the norm is the low half.
+  // the norm descriptor covers the aligned words holding the row's norms
+  // (never past the norm region: its end is 64-byte aligned).
   const uint32_t lane_idx = (uint32_t)(rs * row_bytes + li * kCB);
   const uint32_t lane_nrm = (uint32_t)(li >> 2) * 2u;                 // FULL: rs == 0
   auto issue = [&](int k, int part, Chunk<IB> (&dst)[CPL], uint32_t (&ndst)[CPL]) {
@@ -375,17 +374,17 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
     const int sbase = (si * nparts + part) * CPL;                // first slot of the item
     if constexpr (FULL) {
       const uint32_t nrow = (uint32_t)rbase * (uint32_t)ng;       // the row's first norm
-      const uint32_t adj = (nrow & 1u) * 2u;
+      const uint32_t adj = (nrow & 1u) * 2u;                      // its byte offset in its word
       const __amdgpu_buffer_rsrc_t ri =
           make_rsrc(A.idx + (size_t)rbase * row_bytes, live ? (uint32_t)row_bytes : 0u);
       const __amdgpu_buffer_rsrc_t rn =
-          make_rsrc(A.norms + (nrow & ~1u), live ? (uint32_t)(2 * ng + 2) + adj : 0u);
+          make_rsrc(A.norms + (nrow & ~1u), live ? ((uint32_t)(2 * ng) + adj + 3u) & ~3u : 0u);
       const uint32_t oi = lane_idx + (uint32_t)(sbase * P * kCB);
       const uint32_t on = lane_nrm + adj + (uint32_t)(sbase * (P / 2));
 #pragma unroll
       for (int m = 0; m < CPL; ++m) {
         dst[m] = load_chunk<IB>(ri, oi + (uint32_t)(m * P * kCB));
-        ndst[m] = __builtin_amdgcn_raw_buffer_load_b32(rn, on + (uint32_t)(m * (P / 2)), 0, 0);
+        ndst[m] = load_norm_word(rn, on + (uint32_t)(m * (P / 2)));
       }
       return;
     }
@@ -617,7 +616,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
     const int sbase = (si * nparts + ppart) * CPL;
     // which half of the norm word: parity of the chunk's group index (for P = 64
     // the same for all CPL chunks: their groups differ by multiples of 16)
-    const uint32_t nsh = FULL ? 0u : (uint32_t)((row * ng + ((li + P * sbase) >> 2)) & 1) * 16u;
+    const uint32_t nsh = (uint32_t)((row * ng + ((li + P * sbase) >> 2)) & 1) * 16u;
     // software pipeline over the item's chunks: the lookups of chunk m+1 are
     // in flight while chunk m's dot products run; sched_barrier keeps the
     // compiler from hoisting further (which would blow the register budget)

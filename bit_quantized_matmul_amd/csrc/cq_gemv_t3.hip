@@ -233,7 +233,7 @@ bool cq_gemv_t3_supported(const bqm_cq_layout &L, int batch) {
   const int ng = L.cols / kGroup;
   const int max_groups = batch == 1 ? kT3MaxGroups : kT3MaxGroupsBatched;
   return batch >= 1 && batch <= 16 && L.group == kGroup && L.cols % kGroup == 0 && ng >= 1 &&
-         ng <= max_groups && L.total_bytes < ((int64_t)1 << 31);
+         (ng <= max_groups || cq_t3_mma_supported(L, batch)) && L.total_bytes < ((int64_t)1 << 31);
 }
 
 namespace {
@@ -273,8 +273,10 @@ hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const 
   if (batch == 1)
     return L.cols / kGroup > 64 ? launch_t3<2, 1>(blob, L, T, q, scale, y, num_cus, s)
                                 : launch_t3<1, 1>(blob, L, T, q, scale, y, num_cus, s);
-  // several tokens (rows of at most 64 groups): launches of 4, 2 and 1 tokens,
-  // each one pass over the weights
+  // several tokens: one pass over the weights on the int8 matrix cores
+  if (cq_t3_mma_supported(L, batch)) return launch_cq_t3_mma(blob, L, T, q, scale, batch, y, num_cus, s);
+  // (rows of at most 64 groups) launches of 4, 2 and 1 tokens, each one pass
+  // over the weights
   for (int b0 = 0; b0 < batch;) {
     const int nb = batch - b0 >= 4 ? 4 : (batch - b0 >= 2 ? 2 : 1);
     const int8_t *qb = q + (size_t)b0 * L.cols;

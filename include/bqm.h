@@ -123,10 +123,13 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * launch.  The VALU and matrix-core routes form every product level x code
  * exactly, so each y[b, n] is within a few units of fp32 roundoff of
  * scale[b] / G * sum_g norm[n, g] * sum_i |cb[idx[n, i]]| * |q[b, i]|.
- * Base-3 ternary (bits 6): batch 1 with cols <= 16384, or 2 <= batch <= 16
- * with cols <= 8192 (BQM_ENOTSUP otherwise), on the VALU path in launches of
- * up to 4 tokens; the group sums of digit x code are exact int32 dot
- * products, scaled by the fp32 norm and summed in fp32. */
+ * Base-3 ternary (bits 6): 1 <= batch <= 16 with cols <= 16384 (BQM_ENOTSUP
+ * otherwise); one token on the VALU kernel (int8 dot products), 2..16 tokens
+ * in one pass over the weights on the int8 matrix cores.  Either way the
+ * group sums of (digit - 1) x code are exact int32 sums, scaled by the fp32
+ * norm and summed over the groups in fp32 (in another order on each route,
+ * so a token's y from a batched call equals its one-token y only to fp32
+ * roundoff). */
 int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int batch, float *y, bqm_stream_t stream);
 
@@ -197,9 +200,12 @@ int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const flo
  * |q[m, i]| of the exact sum, at any scale of the row.  Activations enter as
  * exact fp16 integers; the matrix cores accumulate in fp32 and the token
  * scale is applied in fp32.  m >= 1, group must be 128.
+ * Base-3 ternary (bits 6): the cq_gemv product on each 16 tokens (exact
+ * int32 group sums on the int8 matrix cores, fp32 norms; a last single token
+ * on the VALU kernel), so the weights are read once per 16 tokens; cols <=
+ * 16384 (BQM_ENOTSUP otherwise), any m.
  * Returns BQM_ENOTSUP when the packed indices or m * cols exceed 2^30 bytes
- * (the kernel addresses them with 32-bit offsets), and for base-3 ternary
- * (bits 6), which has a decode product only. */
+ * (the kernel addresses them with 32-bit offsets). */
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook,
             const int8_t *q, const float *scale, int m, float *y, bqm_stream_t stream);
 

@@ -102,13 +102,15 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv(p, ctypes.byref(wide), cb, p, p, 1, p, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
-    # base-3 ternary: batch 1 only, no GEMM, the fused path needs the code buffers
+    # base-3 ternary: up to 16 tokens and 128 groups a row (the GEMM likewise,
+    # 16 tokens a pass), the fused path needs the code buffers
     t3 = binding.cq_pack_info(256, 512, 128, 6)
     assert lib.cq_gemv(p, ctypes.byref(t3), cb, p, p, 1, p, None) == E.BQM_EINVAL      # analytic: NULL
     assert lib.cq_gemv(p, ctypes.byref(t3), None, p, p, 17, p, None) == E.BQM_ENOTSUP
-    t3wide = binding.cq_pack_info(8, 8320, 128, 6)                                    # 65 groups
-    assert lib.cq_gemv(p, ctypes.byref(t3wide), None, p, p, 2, p, None) == E.BQM_ENOTSUP  # several tokens: <= 64
-    assert lib.cq_gemm(p, ctypes.byref(t3), None, p, p, 4, p, None) == E.BQM_ENOTSUP
+    t3wide = binding.cq_pack_info(8, 16512, 128, 6)                                   # 129 groups
+    assert lib.cq_gemv(p, ctypes.byref(t3wide), None, p, p, 2, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemm(p, ctypes.byref(t3wide), None, p, p, 4, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemm(p, ctypes.byref(t3), cb, p, p, 4, p, None) == E.BQM_EINVAL      # analytic: NULL
     assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, None, None, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, ctypes.c_void_p(4100), p, None) == E.BQM_EALIGN
     t3big = binding.cq_pack_info(8, 16512, 128, 6)                                      # 129 groups
