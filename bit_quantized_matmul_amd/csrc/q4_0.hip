@@ -16,7 +16,10 @@
 // closes with a butterfly across the P lanes (no LDS, no second barrier).
 // An 18-byte block is fetched as the 16 bytes from the 4-byte-aligned address
 // below it plus the next 4 (2 for a final block that ends there), then
-// realigned with v_alignbyte.
+// realigned with v_alignbyte.  Rows of 9 to 16 blocks (every Minueza matrix
+// but the down projections) take a second kernel with no LDS and no barrier:
+// 16 lanes a row, each lane's activations in registers, row tiles walked by a
+// persistent grid (q4_0_gemv_rows_kernel below).
 #include "bqm_common.h"
 #include "q4_0_block.h"
 
@@ -285,8 +288,9 @@ hipError_t launch_batch(const uint8_t *blocks, int rows, int cols, int nblk, uin
   // lanes per row: the power of two covering the row's blocks (4 .. 64)
   int P = 4;
   while (P < 64 && P < nblk) P *= 2;
-  // tall matrices of 9 to 16 blocks a row: persistent row tiles
-  if (P == 16 && rows >= num_cus * (kThreads / 16) * 2) {
+  // rows of 9 to 16 blocks: row tiles with the activations in registers (a
+  // persistent grid for tall matrices, one tile a workgroup for short ones)
+  if (P == 16) {
     const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
     return vec ? launch_rows<BATCH, true>(blocks, rows, cols, nblk, total, x, y, num_cus, s)
                : launch_rows<BATCH, false>(blocks, rows, cols, nblk, total, x, y, num_cus, s);
