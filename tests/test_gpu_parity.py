@@ -276,7 +276,9 @@ def test_q4_0_gemv_parity(rows, cols, batch):
 # buffer (512 cols), ragged ones with cols % 4 != 0 (301, 318: 4-byte
 # activation loads), and batches split 4+1, 2+1 and 4+2
 @pytest.mark.parametrize("rows,cols,batch", [(8192, 512, 1), (9001, 301, 3), (32002, 312, 5),
-                                             (8200, 318, 6)])
+                                             (8200, 318, 6),
+                                             # fewer rows than a 16-row tile, a ragged last tile
+                                             (5, 300, 2), (17, 500, 3), (1, 289, 1)])
 def test_q4_0_gemv_row_tiles(rows, cols, batch):
     rng = np.random.default_rng(610 + rows + cols + batch)
     w = inputs.weight_matrix(rng, rows, cols)
