@@ -49,6 +49,7 @@ typedef int i32x4m __attribute__((ext_vector_type(4)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2m __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3m __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc3(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -137,7 +138,9 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
   // codes of chunk c: lane (h, l16) takes token l16's codes 40 h .. 40 h + 39
   // of each group of the eighth (the digits of bytes 8 h .. 8 h + 7); codes
   // past the group's 128 read as zeros, and so do tokens past the batch
-  typedef u32x2m Raw[PD][5];
+  // (16 + 16 + 8 bytes a group; lane h = 3 keeps only the first 8 of its
+  // first 16, the rest being the next group's)
+  typedef uint32_t Raw[PD][10];
   auto load_codes = [&](Raw &qraw, int c) {
     int g0, ngw;
     eighth(c, g0, ngw);
@@ -145,10 +148,16 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
     for (int j = 0; j < PD; ++j) {
       const int g = g0 + j < ng ? g0 + j : ng - 1;
       const uint32_t off = (uint32_t)(l16 * K + g * kGroup + 40 * h);
-#pragma unroll
-      for (int u = 0; u < 5; ++u)
-        qraw[j][u] = __builtin_bit_cast(u32x2m, __builtin_amdgcn_raw_buffer_load_b64(
-                                                    rq, 40 * h + 8 * u < kGroup ? off + 8u * u : kOOB3, 0, 0));
+      const bool tail = h == 3;                    // codes 120 .. 127 only
+      const u32x4m a0 = __builtin_bit_cast(u32x4m, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      const u32x4m a1 = __builtin_bit_cast(u32x4m, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rq, tail ? kOOB3 : off + 16u, 0, 0));
+      const u32x2m a2 = __builtin_bit_cast(u32x2m, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rq, tail ? kOOB3 : off + 32u, 0, 0));
+      qraw[j][0] = a0.x; qraw[j][1] = a0.y;
+      qraw[j][2] = tail ? 0u : a0.z; qraw[j][3] = tail ? 0u : a0.w;
+      qraw[j][4] = a1.x; qraw[j][5] = a1.y; qraw[j][6] = a1.z; qraw[j][7] = a1.w;
+      qraw[j][8] = a2.x; qraw[j][9] = a2.y;
     }
   };
   // as A fragments: step s holds bytes 2 s and 2 s + 1 of the lane's eight,
@@ -160,10 +169,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
     for (int j = 0; j < PD; ++j) {
       uint32_t d[10];
 #pragma unroll
-      for (int u = 0; u < 5; ++u) {
-        d[2 * u] = qraw[j][u].x;
-        d[2 * u + 1] = qraw[j][u].y;
-      }
+      for (int u = 0; u < 10; ++u) d[u] = qraw[j][u];
       a[j][0] = i32x4m{(int)get4<0>(d), (int)get1<4>(d), (int)get4<5>(d), (int)get1<9>(d)};
       a[j][1] = i32x4m{(int)get4<10>(d), (int)get1<14>(d), (int)get4<15>(d), (int)get1<19>(d)};
       a[j][2] = i32x4m{(int)get4<20>(d), (int)get1<24>(d), (int)get4<25>(d), (int)get1<29>(d)};
@@ -174,11 +180,12 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
   // a ring: tile tt's weight bytes of the lane (row l16 of block rb0 + tt %
   // NRB, groups g0 + j of chunk tt / NRB: the 12 bytes from the 4-byte-aligned
   // address at or below byte 8 h of the group, realigned at use) and its
-  // row's norm of each group (the aligned word holding it).
+  // row's norms of the PD groups (the NW aligned words holding them, one load).
   // Past the matrix or the tiles the loads read zeros; past the eighth's
   // groups they read whatever lies there and the norm is taken as zero.
   typedef uint32_t Ring[PD][3];
-  typedef uint32_t NRing[PD];
+  constexpr int NW = (PD + 2) / 2;
+  typedef uint32_t NRing[NW];
   auto issue = [&](Ring &w, NRing &n, int tt) {
     int g0, ngw;
     eighth(tt / NRB, g0, ngw);
@@ -189,7 +196,17 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
       const uint32_t off = (uint32_t)row * row_bytes + (uint32_t)(g0 + j) * kTritBytes + 8u * h;
       const u32x3m v = __builtin_bit_cast(u32x3m, __builtin_amdgcn_raw_buffer_load_b96(rw, ok ? off & ~3u : kOOB3, 0, 2));
       w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z;
-      n[j] = __builtin_amdgcn_raw_buffer_load_b32(rn, ok ? (((uint32_t)row * ng + g0 + j) * 2u) & ~3u : kOOB3, 0, 0);
+    }
+    // a word past the norm region (the region ends 64-byte aligned) reads 0
+    const uint32_t nb = ok ? (((uint32_t)row * ng + g0) * 2u) & ~3u : kOOB3;
+    if constexpr (NW == 3) {
+      const u32x3m v = __builtin_bit_cast(u32x3m, __builtin_amdgcn_raw_buffer_load_b96(rn, nb, 0, 0));
+      n[0] = v.x; n[1] = v.y; n[2] = v.z;
+    } else if constexpr (NW == 2) {
+      const u32x2m v = __builtin_bit_cast(u32x2m, __builtin_amdgcn_raw_buffer_load_b64(rn, nb, 0, 0));
+      n[0] = v.x; n[1] = v.y;
+    } else {
+      n[0] = __builtin_amdgcn_raw_buffer_load_b32(rn, nb, 0, 0);
     }
   };
 
@@ -200,6 +217,13 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
     eighth(tt / NRB, g0, ngw);
     const int i = tt % NRB;
     const int row = (rb0 + i) * 16 + l16;
+    // the norms' halves from group g0 on: the first sits in the high half of
+    // word 0 when the row's norms start 2 bytes into a word
+    const uint32_t p = ((uint32_t)row * ng + g0) & 1u;
+    uint32_t nh[(PD + 1) / 2];
+#pragma unroll
+    for (int m = 0; m < (PD + 1) / 2; ++m)
+      nh[m] = m + 1 < NW ? __builtin_amdgcn_alignbit(n[m + 1], n[m], p * 16u) : n[m] >> (p * 16u);
     f32x4m tot = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
@@ -212,8 +236,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][1], digits_step<1>(w0, w1, tab, lo), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][2], digits_step<2>(w0, w1, tab, lo), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][3], digits_step<3>(w0, w1, tab, lo), acc, 0, 0, 0);
-      const uint32_t nsh = (((uint32_t)row * ng + g0 + j) & 1u) * 16u;
-      const float nv = j < ngw ? half_bits_to_float((uint16_t)(n[j] >> nsh)) : 0.0f;
+      const float nv = j < ngw ? half_bits_to_float((uint16_t)(nh[j >> 1] >> ((j & 1) * 16))) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) tot[r] = fmaf(nv, (float)acc[r], tot[r]);
     }
@@ -233,11 +256,21 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
 #pragma unroll
   for (int r = 0; r < R; ++r) issue(wr[r], nr[r], r);
 
-  // the digit table: 16 bytes a store, two copies of one entry
+  // the digit table: 16 bytes a store, two copies of one entry.  Store i of
+  // thread t writes row v = t / 16 + 32 i; the wave's 32 rows (4 wave + r +
+  // 32 i, r < 4) are computed once, by lane 4 i + r (and again by lane
+  // 32 + 4 i + r), and fetched from there with ds_bpermute.
+  static_assert(kTab3 == 8 * kThreads3 * 16, "eight 16-byte stores a thread");
+  {
+    const int lv = lane & 31;
+    const uint2 mine = digit_entry((uint32_t)(4 * wave + (lv & 3) + 32 * (lv >> 2)));
 #pragma unroll
-  for (int o = t * 16; o < kTab3; o += kThreads3 * 16) {
-    const uint2 e = digit_entry((uint32_t)(o >> 8));
-    *reinterpret_cast<uint4 *>(tab + o) = make_uint4(e.x, e.y, e.x, e.y);
+    for (int i = 0; i < 8; ++i) {
+      const int src = (4 * i + (lane >> 4)) << 2;
+      const uint32_t e0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.x);
+      const uint32_t e1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.y);
+      *reinterpret_cast<uint4 *>(tab + t * 16 + i * kThreads3 * 16) = make_uint4(e0, e1, e0, e1);
+    }
   }
   convert(qraw);
   if (CHUNKED) load_codes(qraw, 1);
