@@ -373,19 +373,20 @@ def bench_prefill(B, torch, dev, cbs, steps, warmup):
         out[label] = dict(m=int(q.shape[0]), us=ms * 1e3, us_repeats=spread(times), tflops=tf,
                           frac=tf / MFMA_F16_PEAK_TFLOPS)
         del blob, y
-    # base-3 ternary at the wide shape: the 16-token matrix-core product per
-    # 16 tokens (weights read once a pass; int8 MFMA at 208 of 256 k slots)
+    # base-3 ternary at the wide shape: the base-3 GEMM (int8 MFMA, 8 k slots
+    # a weight byte: 130 real of 224 slots a group; frac counts real MACs)
     label, w = wl.weights[0]
     rows, cols = w.shape
     lay = B.cq_pack_info(rows, cols, 128, 6)
     blob = B.cq_pack(torch.from_numpy(w).to(dev), lay, None)
     y = torch.empty((q.shape[0], rows), dtype=torch.float32, device=dev)
     B.cq_gemm(blob, lay, None, q, s, y=y)
-    times = graph_repeats_ms(torch, [(lambda: B.cq_gemm(blob, lay, None, q, s, y=y)) for _ in range(5)], repeats=3)
+    times = graph_repeats_ms(torch, [(lambda: B.cq_gemm(blob, lay, None, q, s, y=y))
+                                     for _ in range(max(steps, 10))], repeats=5)
     ms = sorted(times)[len(times) // 2]
     tf = 2.0 * q.shape[0] * rows * cols / ms / 1e9
     out[f"ternary_base3_{label}"] = dict(m=int(q.shape[0]), us=ms * 1e3, us_repeats=spread(times), tops=tf,
-                                         frac_int8_peak=tf / INT8_MFMA_PEAK_TOPS, passes=(q.shape[0] + 15) // 16)
+                                         frac_int8_peak=tf / INT8_MFMA_PEAK_TOPS)
     del blob, y
     # context: the dense fp16 GEMM the format avoids (hipBLASLt via torch.mm,
     # contiguous [M, K] x [K, N] operands, fp16 weights of the same shape)

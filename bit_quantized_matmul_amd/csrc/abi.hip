@@ -339,30 +339,26 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
   // the kernel addresses the weights and activations with 32-bit offsets;
-  // base-3 ternary runs its 16-token matrix-core product per 16 tokens
+  // base-3 ternary: up to 16 tokens (and up to 16384 columns) run the batched
+  // decode kernels, more on the base-3 GEMM
   const bool base3 = layout->bits == BQM_CQ_TERNARY_B3;
+  const bool base3_small = base3 && m <= 16 && cq_t3_mma_supported(*layout, 2);
   if (layout->idx_bytes >= (int64_t)1 << 30 || (int64_t)m * layout->cols >= (int64_t)1 << 30 ||
-      (base3 && !cq_t3_mma_supported(*layout, 2)))
+      (base3 && !base3_small && !cq_t3_gemm_supported(*layout, m)))
     return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;
   int cus;
   rc = current_device(&cus);
   if (rc) return rc;
-  if (base3) {
-    for (int t0 = 0; t0 < m; t0 += 16) {
-      const int nb = m - t0 < 16 ? m - t0 : 16;
-      const int8_t *qb = q + (size_t)t0 * layout->cols;
-      float *yb = y + (size_t)t0 * layout->rows;
-      const hipError_t e =
-          nb >= 2 ? launch_cq_t3_mma((const uint8_t *)blob, *layout, T, qb, scale + t0, nb, yb, cus,
-                                     (hipStream_t)stream)
-                  : launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, qb, scale + t0, 1, yb, cus,
-                                      (hipStream_t)stream);
-      if (e != hipSuccess) return status_of(e);
-    }
-    return BQM_OK;
-  }
+  if (base3_small)
+    return status_of(m >= 2 ? launch_cq_t3_mma((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
+                                               (hipStream_t)stream)
+                            : launch_cq_gemv_t3((const uint8_t *)blob, *layout, T, q, scale, 1, y, cus,
+                                                (hipStream_t)stream));
+  if (base3)
+    return status_of(launch_cq_t3_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
+                                       (hipStream_t)stream));
   return status_of(launch_cq_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
                                   (hipStream_t)stream));
 }

@@ -126,6 +126,11 @@ bool cq_t3_mma_supported(const bqm_cq_layout &L, int batch);
 hipError_t launch_cq_t3_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                             const int8_t *q, const float *scale, int batch, float *y, int num_cus,
                             hipStream_t s);
+// Base-3 prefill GEMM: any m, any column count (group 128).
+bool cq_t3_gemm_supported(const bqm_cq_layout &L, int m);
+hipError_t launch_cq_t3_gemm(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                             const int8_t *q, const float *scale, int m, float *y, int num_cus,
+                             hipStream_t s);
 hipError_t launch_cq_gemv_t3(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                              const int8_t *q, const float *scale, int batch, float *y, int num_cus,
                              hipStream_t s);

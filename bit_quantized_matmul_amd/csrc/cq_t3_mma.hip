@@ -97,6 +97,23 @@ __device__ __forceinline__ uint32_t get1(const uint32_t (&d)[10]) {
   return (d[O >> 2] >> (8 * (O & 3))) & 0xFFu;
 }
 
+// The digit table of a 512-thread workgroup: 16 bytes a store, two copies
+// of one entry.  Store i of thread t writes row v = t / 16 + 32 i; the wave's
+// 32 rows (4 wave + r + 32 i, r < 4) are computed once, by lane 4 i + r (and
+// again by lane 32 + 4 i + r), and fetched from there with ds_bpermute.
+static_assert(kTab3 == 8 * kThreads3 * 16, "eight 16-byte stores a thread");
+__device__ __forceinline__ void build_digit_table(uint8_t *tab, int t) {
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6), lv = lane & 31;
+  const uint2 mine = digit_entry((uint32_t)(4 * wave + (lv & 3) + 32 * (lv >> 2)));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int src = (4 * i + (lane >> 4)) << 2;
+    const uint32_t e0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.x);
+    const uint32_t e1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.y);
+    *reinterpret_cast<uint4 *>(tab + t * 16 + i * kThreads3 * 16) = make_uint4(e0, e1, e0, e1);
+  }
+}
+
 struct T3MmaArgs {
   const uint8_t *blob;
   const uint16_t *norms;
@@ -256,22 +273,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
 #pragma unroll
   for (int r = 0; r < R; ++r) issue(wr[r], nr[r], r);
 
-  // the digit table: 16 bytes a store, two copies of one entry.  Store i of
-  // thread t writes row v = t / 16 + 32 i; the wave's 32 rows (4 wave + r +
-  // 32 i, r < 4) are computed once, by lane 4 i + r (and again by lane
-  // 32 + 4 i + r), and fetched from there with ds_bpermute.
-  static_assert(kTab3 == 8 * kThreads3 * 16, "eight 16-byte stores a thread");
-  {
-    const int lv = lane & 31;
-    const uint2 mine = digit_entry((uint32_t)(4 * wave + (lv & 3) + 32 * (lv >> 2)));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int src = (4 * i + (lane >> 4)) << 2;
-      const uint32_t e0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.x);
-      const uint32_t e1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.y);
-      *reinterpret_cast<uint4 *>(tab + t * 16 + i * kThreads3 * 16) = make_uint4(e0, e1, e0, e1);
-    }
-  }
+  build_digit_table(tab, t);
   convert(qraw);
   if (CHUNKED) load_codes(qraw, 1);
   __syncthreads();
@@ -320,6 +322,238 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
   }
 }
 
+// ------------------------------------------------------------------- GEMM
+//
+// Prefill: m tokens against the whole matrix, the weights read once per
+// workgroup tile rather than once per 16 tokens.  v_mfma_i32_32x32x32_i8:
+// A = 32 tokens x 32 k slots, B = 32 k slots x 32 weight rows, 16 slots (two
+// weight bytes, five digits and three zeros each) a lane.  A group's 26 bytes
+// and two more (past its end, meeting zero codes) are 7 steps of 4 bytes:
+// lane half h takes bytes 14 h .. 14 h + 13, bytes 14 h + 2 s and + 1 in
+// step s.  The int32 group sums are exact (|.| <= 128 * 127), scaled by the
+// row's fp32 norm and added in fp32 once per group, in group order.
+//  * Workgroup tile 64 MB tokens x 128 NB rows: eight waves, two along the
+//    tokens and four along the rows, each 32 MB x 32 NB (MB x NB MFMA
+//    tiles).  Every wave runs all of K.
+//  * The tokens' codes of one group are staged once per workgroup in LDS,
+//    already laid out as A operands: per token 28 eight-byte slot groups (five
+//    codes, three zeros; the codes past the group's 128 zero), 240 bytes a
+//    token (an odd multiple of 16: the b128 fragment reads of 32 tokens fall
+//    on distinct banks).  Two buffers: group g + 1 is staged while g is
+//    multiplied, one barrier a group.
+//  * Weights: a lane loads its row's 14 bytes of a group as the 20 bytes from
+//    the 4-byte-aligned address below them (realigned with v_alignbyte),
+//    two groups ahead, with the row's norm word.
+constexpr int kT3GSlots = 28;              // slot groups (weight bytes) a group
+constexpr int kT3GStride = 240;            // LDS bytes a token row of an A buffer
+constexpr int kT3GSteps = 7;               // MFMA steps a group
+typedef int i32x16m __attribute__((ext_vector_type(16)));
+
+struct T3GemmArgs {
+  const uint8_t *blob;
+  const uint16_t *norms;
+  const int8_t *q;
+  const float *scale;
+  float *y;
+  int m, rows, cols, tiles_m, tiles_n;
+  uint32_t blob_bytes, norm_bytes, q_bytes;
+  float cfac;
+};
+
+template <int MB, int NB>
+__global__ __launch_bounds__(kThreads3) void cq_t3_gemm_kernel(T3GemmArgs A) {
+  constexpr int BM = 64 * MB, BN = 128 * NB;
+  constexpr int kABuf = BM * kT3GStride;
+  constexpr int kItems = BM * 7;                   // A staging items: 20 codes (4 slot groups) each
+  constexpr int kIt = (kItems + kThreads3 - 1) / kThreads3;
+  static_assert(kTab3 + 2 * kABuf <= 163840, "LDS of one CU");
+  __shared__ __align__(16) uint8_t lds[kTab3 + 2 * kABuf];
+  uint8_t *const tab = lds;
+  uint8_t *const abuf = lds + kTab3;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // XCD-aware tile order: the m-tiles of one n-block (which share weights)
+  // are consecutive tiles and run on one XCD
+  const int ntiles = A.tiles_m * A.tiles_n;
+  const int per = (ntiles + 7) / 8;
+  const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (tile >= ntiles) return;
+  const int mt = tile % A.tiles_m, nt = tile / A.tiles_m;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int K = A.cols, N = A.rows, ng = K / kGroup;
+  const uint32_t row_bytes = (uint32_t)ng * kTritBytes;
+  const __amdgpu_buffer_rsrc_t rw = rsrc3(A.blob, A.blob_bytes);
+  const __amdgpu_buffer_rsrc_t rn = rsrc3(A.norms, A.norm_bytes);
+  const __amdgpu_buffer_rsrc_t rq = rsrc3(A.q, A.q_bytes);
+
+  // A staging: item i is token i / 7, codes 20 p .. 20 p + 19 (p = i % 7) of
+  // the group, i.e. slot groups 4 p .. 4 p + 3; codes 128 .. 139 (p = 6,
+  // dwords 2..4) are zero.  Rows past m and groups past K read zeros.
+  uint32_t qoff[kIt];
+  int iwhere[kIt];                                 // LDS byte offset of the item's 32 bytes, -1: none
+  bool itail[kIt];
+#pragma unroll
+  for (int u = 0; u < kIt; ++u) {
+    const int i = t + u * kThreads3;
+    const int tl = i / 7, p = i - 7 * (i / 7);
+    const bool ok = i < kItems;
+    iwhere[u] = ok ? tl * kT3GStride + 32 * p : -1;
+    itail[u] = p == 6;
+    qoff[u] = ok && m0 + tl < A.m ? (uint32_t)(m0 + tl) * (uint32_t)K + 20u * p : kOOB3;
+  }
+  uint32_t araw[kIt][5];
+  auto load_a = [&](int g) {
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      const uint32_t off = g < ng && qoff[u] != kOOB3 ? qoff[u] + (uint32_t)g * kGroup : kOOB3;
+      const u32x4m v = __builtin_bit_cast(u32x4m, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      araw[u][0] = v.x; araw[u][1] = v.y; araw[u][2] = v.z; araw[u][3] = v.w;
+      araw[u][4] = __builtin_amdgcn_raw_buffer_load_b32(rq, off + 16u, 0, 0);
+    }
+  };
+  auto stage_a = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      if (iwhere[u] < 0) continue;
+      const uint32_t d0 = araw[u][0], d1 = araw[u][1];
+      const uint32_t d2 = itail[u] ? 0u : araw[u][2], d3 = itail[u] ? 0u : araw[u][3];
+      const uint32_t d4 = itail[u] ? 0u : araw[u][4];
+      const uint4 lo = make_uint4(d0, d1 & 0xFFu, __builtin_amdgcn_alignbyte(d2, d1, 1), (d2 >> 8) & 0xFFu);
+      const uint4 hi = make_uint4(__builtin_amdgcn_alignbyte(d3, d2, 2), (d3 >> 16) & 0xFFu,
+                                  __builtin_amdgcn_alignbyte(d4, d3, 3), d4 >> 24);
+      uint8_t *dst = abuf + buf * kABuf + iwhere[u];
+      *reinterpret_cast<uint4 *>(dst) = lo;
+      *reinterpret_cast<uint4 *>(dst + 16) = hi;
+    }
+  };
+
+  // B: row n = n0 + 32 (NB wn + nb) + lr of each n-block nb; its 14 bytes of
+  // group g from 26 g + 14 lh, and the word holding its norm
+  uint32_t wbase[NB], nidx[NB];
+  bool nok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + 32 * (NB * wn + nb) + lr;
+    nok[nb] = n < N;
+    wbase[nb] = (uint32_t)n * row_bytes + 14u * lh;
+    nidx[nb] = (uint32_t)n * (uint32_t)ng;
+  }
+  uint32_t wraw[2][NB][5], nraw[2][NB];
+  auto load_b = [&](int g, int slot) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bool ok = nok[nb] && g < ng;
+      const uint32_t off = ok ? (wbase[nb] + (uint32_t)g * kTritBytes) & ~3u : kOOB3;
+      const u32x4m v = __builtin_bit_cast(u32x4m, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+      wraw[slot][nb][0] = v.x; wraw[slot][nb][1] = v.y; wraw[slot][nb][2] = v.z; wraw[slot][nb][3] = v.w;
+      wraw[slot][nb][4] = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 16u, 0, 0);
+      nraw[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(rn, ok ? ((nidx[nb] + (uint32_t)g) * 2u) & ~3u : kOOB3, 0, 0);
+    }
+  };
+
+  float tot[MB][NB][16];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[mb][nb][r] = 0.0f;
+
+  const uint32_t lo = (uint32_t)lr * 8u;
+  // lane's A fragment rows: tokens 32 (MB wm + mb) + lr, slot groups 14 lh + 2 s, + 1
+  const int afrag = (32 * MB * wm + lr) * kT3GStride + 112 * lh;
+  auto mult = [&](int g, int slot) {
+    uint32_t wd[NB][4];
+    float nv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t sh = (wbase[nb] + (uint32_t)g * kTritBytes) & 2u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wd[nb][e] = __builtin_amdgcn_alignbyte(wraw[slot][nb][e + 1], wraw[slot][nb][e], sh);
+      nv[nb] = half_bits_to_float((uint16_t)(nraw[slot][nb] >> (((nidx[nb] + (uint32_t)g) & 1u) * 16u)));
+    }
+    const uint8_t *ab = abuf + (g & 1) * kABuf + afrag;
+    i32x16m acc[MB][NB];
+#pragma unroll
+    for (int s = 0; s < kT3GSteps; ++s) {
+      i32x4m af[MB], bf[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const i32x4m *>(ab + 32 * mb * kT3GStride + 16 * s);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t w = wd[nb][s >> 1];
+        const uint2 e0 = *reinterpret_cast<const uint2 *>(tab + ((s & 1) ? taddr3<2>(w, lo) : taddr3<0>(w, lo)));
+        const uint2 e1 = *reinterpret_cast<const uint2 *>(tab + ((s & 1) ? taddr3<3>(w, lo) : taddr3<1>(w, lo)));
+        bf[nb] = i32x4m{(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              af[mb], bf[nb], s == 0 ? i32x16m{} : acc[mb][nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tot[mb][nb][r] = fmaf(nv[nb], (float)acc[mb][nb][r], tot[mb][nb][r]);
+  };
+
+  load_a(0);
+  load_b(0, 0);
+  load_b(1, 1);
+  build_digit_table(tab, t);
+  stage_a(0);
+  load_a(1);
+  __syncthreads();
+  // group g: stage g + 1 (its codes loaded during g - 1), load the codes of
+  // g + 2, multiply g, load the weights of g + 2 into g's ring slot
+  for (int g0 = 0; g0 < ng; g0 += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int g = g0 + d;
+      if (g < ng) {
+        stage_a((g + 1) & 1);
+        load_a(g + 2);
+        mult(g, d);
+        load_b(g + 2, d);
+      }
+      __syncthreads();
+    }
+  }
+
+  // D layout: register r of a lane holds token 8 (r / 4) + 4 lh + r % 4,
+  // row lr of its 32 x 32 tile
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * (MB * wm + mb) + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (m >= A.m) continue;
+      const float f = A.scale[m] * A.cfac;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = n0 + 32 * (NB * wn + nb) + lr;
+        if (n < N) A.y[(size_t)m * N + n] = tot[mb][nb][r] * f;
+      }
+    }
+}
+
+template <int MB, int NB>
+hipError_t launch_t3_gemm_tiles(T3GemmArgs A, hipStream_t s) {
+  A.tiles_m = (A.m + 64 * MB - 1) / (64 * MB);
+  A.tiles_n = (A.rows + 128 * NB - 1) / (128 * NB);
+  const int grid = ((A.tiles_m * A.tiles_n + 7) / 8) * 8;
+  cq_t3_gemm_kernel<MB, NB><<<grid, kThreads3, 0, s>>>(A);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool cq_t3_mma_supported(const bqm_cq_layout &L, int batch) {
@@ -364,6 +598,36 @@ hipError_t launch_cq_t3_mma(const uint8_t *blob, const bqm_cq_layout &L, const L
   if (pd_need > 2) return with_nrb(std::integral_constant<int, 4>{}, std::false_type{});
   if (pd_need > 1) return with_nrb(std::integral_constant<int, 2>{}, std::false_type{});
   return with_nrb(std::integral_constant<int, 1>{}, std::false_type{});
+}
+
+bool cq_t3_gemm_supported(const bqm_cq_layout &L, int m) {
+  return m >= 1 && L.group == kGroup && L.cols % kGroup == 0 && L.total_bytes < ((int64_t)1 << 31) &&
+         (int64_t)m * L.cols < ((int64_t)1 << 31) - 64;
+}
+
+// Tile shape: the largest of 128 x 256, 128 x 128, 64 x 128 (tokens x rows)
+// whose tile count still covers 7/8 of the CUs, else 64 x 128.
+hipError_t launch_cq_t3_gemm(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                             const int8_t *q, const float *scale, int m, float *y, int num_cus,
+                             hipStream_t s) {
+  T3GemmArgs A{};
+  A.blob = blob;
+  A.norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
+  A.q = q;
+  A.scale = scale;
+  A.y = y;
+  A.m = m;
+  A.rows = L.rows;
+  A.cols = L.cols;
+  A.blob_bytes = (uint32_t)L.total_bytes;                     // windows past a row's end stay in the blob
+  A.norm_bytes = (uint32_t)(L.total_bytes - L.norms_offset);   // whole words (64-byte padded)
+  A.q_bytes = (uint32_t)((int64_t)m * L.cols);
+  A.cfac = T.cscale / (float)kGroup;
+  auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((L.rows + bn - 1) / bn); };
+  const long want = (long)num_cus * 7 / 8;
+  if (tiles(128, 256) >= want) return launch_t3_gemm_tiles<2, 2>(A, s);
+  if (tiles(128, 128) >= want) return launch_t3_gemm_tiles<2, 1>(A, s);
+  return launch_t3_gemm_tiles<1, 1>(A, s);
 }
 
 }  // namespace bqm

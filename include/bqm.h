@@ -200,10 +200,11 @@ int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const flo
  * |q[m, i]| of the exact sum, at any scale of the row.  Activations enter as
  * exact fp16 integers; the matrix cores accumulate in fp32 and the token
  * scale is applied in fp32.  m >= 1, group must be 128.
- * Base-3 ternary (bits 6): the cq_gemv product on each 16 tokens (exact
- * int32 group sums on the int8 matrix cores, fp32 norms; a last single token
- * on the VALU kernel), so the weights are read once per 16 tokens; cols <=
- * 16384 (BQM_ENOTSUP otherwise), any m.
+ * Base-3 ternary (bits 6): exact int32 group sums of digit minus one times
+ * code on the int8 matrix cores, each scaled by the group's fp32 norm and
+ * added in fp32 in group order; m <= 16 tokens (with cols <= 16384) run the
+ * cq_gemv kernels, more tokens (or more columns) a GEMM that reads the
+ * weights once per 128 tokens; any m, any cols.
  * Returns BQM_ENOTSUP when the packed indices or m * cols exceed 2^30 bytes
  * (the kernel addresses them with 32-bit offsets). */
 int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook,

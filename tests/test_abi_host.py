@@ -102,14 +102,15 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv(p, ctypes.byref(wide), cb, p, p, 1, p, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
-    # base-3 ternary: up to 16 tokens and 128 groups a row (the GEMM likewise,
-    # 16 tokens a pass), the fused path needs the code buffers
+    # base-3 ternary: the GEMV up to 16 tokens and 128 groups a row (the GEMM
+    # takes any column count, within the 32-bit offsets), the fused path
+    # needs the code buffers
     t3 = binding.cq_pack_info(256, 512, 128, 6)
     assert lib.cq_gemv(p, ctypes.byref(t3), cb, p, p, 1, p, None) == E.BQM_EINVAL      # analytic: NULL
     assert lib.cq_gemv(p, ctypes.byref(t3), None, p, p, 17, p, None) == E.BQM_ENOTSUP
     t3wide = binding.cq_pack_info(8, 16512, 128, 6)                                   # 129 groups
     assert lib.cq_gemv(p, ctypes.byref(t3wide), None, p, p, 2, p, None) == E.BQM_ENOTSUP
-    assert lib.cq_gemm(p, ctypes.byref(t3wide), None, p, p, 4, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemm(p, ctypes.byref(t3wide), None, p, p, 1 << 16, p, None) == E.BQM_ENOTSUP   # m * cols >= 2^30
     assert lib.cq_gemm(p, ctypes.byref(t3), cb, p, p, 4, p, None) == E.BQM_EINVAL      # analytic: NULL
     assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, None, None, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(t3), None, p, 1, p, ctypes.c_void_p(4100), p, None) == E.BQM_EALIGN

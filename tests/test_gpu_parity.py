@@ -506,19 +506,43 @@ def test_cq_gemv_ternary_b3_batched(rows, cols, batch, codebooks):
     assert np.array_equal(yf.view(np.uint32), y2.view(np.uint32))
 
 
-# base-3 prefill: 16 tokens a matrix-core pass, a last pass of 1 token on the VALU kernel
+# base-3 prefill: up to 16 tokens the batched decode launch (bit for bit
+# cq_gemv's), more tokens (or more than 16384 columns) the base-3 GEMM, here
+# in its 64 x 128 tile: ragged token and row tiles, odd group counts, one
+# group, a single token past 16384 columns
 @pytest.mark.parametrize("rows,cols,m", [(300, 512, 37), (129, 4096, 100), (64, 16384, 17), (1000, 384, 16),
-                                         (33, 1024, 1)])
+                                         (33, 1024, 1), (257, 1152, 129), (130, 128, 300), (40, 20480, 20),
+                                         (31, 16512, 1), (500, 2944, 65)])
 def test_cq_gemm_ternary_b3(rows, cols, m, codebooks):
     rng = np.random.default_rng(495 + rows + cols + m)
     lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, ocq.TERNARY_B3, m, codebooks)
     lay = B.cq_pack_info(rows, cols, 128, ocq.TERNARY_B3)
     y = host(B.cq_gemm(dev(blob), lay, None, dev(q), dev(s)))
     P.check_cq(y, idx, n16, 128, ocq.TERNARY_B3, lv, q, s, P.TOL_F32, f"cq_gemm base-3 m{m} {rows}x{cols}")
-    # the same launches as cq_gemv on each 16 tokens: equal bit for bit
-    y16 = host(B.cq_gemv(dev(blob), lay, None, dev(q[:16]), dev(s[:16]))) if m >= 2 else None
-    if y16 is not None:
-        assert np.array_equal(y16.view(np.uint32), y[:min(m, 16)].view(np.uint32))
+    if m <= 16 and cols <= 16384:
+        # the same launch as cq_gemv: equal bit for bit
+        y16 = host(B.cq_gemv(dev(blob), lay, None, dev(q), dev(s)))
+        assert np.array_equal(y16.view(np.uint32), y.view(np.uint32))
+
+
+# the base-3 GEMM's 128 x 256 (m 512, 14336 rows: the bench's prefill line),
+# 128 x 128 and 64 x 128 tiles at full size, ragged in tokens and rows:
+# sampled rows against the oracle
+@pytest.mark.parametrize("m,rows,cols", [(512, 14336, 4096), (256, 14336, 1024), (300, 14000, 2048),
+                                         (512, 4096, 14336)])
+def test_full_size_ternary_b3_prefill_sampled(m, rows, cols):
+    rng = np.random.default_rng(1200 + rows + m + cols)
+    code = ocq.TERNARY_B3
+    w = inputs.weight_matrix(rng, rows, cols, outliers=True)
+    x = inputs.activations(rng, m, cols)
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    blob = B.cq_pack(dev(w), lay, None)
+    q, s = B.act_fwht_quant_a8(dev(x))
+    y = host(B.cq_gemm(blob, lay, None, q, s))
+    sel = np.unique(np.concatenate([sampled_rows(rng, rows, 40), np.arange(rows - 3, rows)]))
+    idx, n16 = ocq.split_blob(host(blob), rows, cols, 128, code)
+    P.check_cq(y[:, sel], idx[sel], n16[sel], 128, code, levels(code, None), host(q), host(s), P.TOL_F32,
+               f"full-size base-3 prefill m{m} {rows}x{cols}")
 
 
 @pytest.mark.parametrize("rows,cols,batch", [(14336, 4096, 16), (4096, 14336, 16), (14336, 4096, 4)])
