@@ -97,20 +97,23 @@ __device__ __forceinline__ uint32_t get1(const uint32_t (&d)[10]) {
   return (d[O >> 2] >> (8 * (O & 3))) & 0xFFu;
 }
 
-// The digit table of a 512-thread workgroup: 16 bytes a store, two copies
-// of one entry.  Store i of thread t writes row v = t / 16 + 32 i; the wave's
-// 32 rows (4 wave + r + 32 i, r < 4) are computed once, by lane 4 i + r (and
-// again by lane 32 + 4 i + r), and fetched from there with ds_bpermute.
-static_assert(kTab3 == 8 * kThreads3 * 16, "eight 16-byte stores a thread");
+// The digit table, built by a workgroup of TH threads (512 or 1024): 16
+// bytes a store, two copies of one entry.  Store i of thread t writes row
+// v = t / 16 + (TH / 16) i; the wave's rows (4 wave + r + (TH / 16) i, r < 4)
+// are computed once, by lane 4 i + r (and again by lane 32 + 4 i + r), and
+// fetched from there with ds_bpermute.
+template <int TH>
 __device__ __forceinline__ void build_digit_table(uint8_t *tab, int t) {
+  static_assert(kTab3 % (TH * 16) == 0 && kTab3 / (TH * 16) <= 8, "at most eight 16-byte stores a thread");
+  constexpr int kStores = kTab3 / (TH * 16);
   const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6), lv = lane & 31;
-  const uint2 mine = digit_entry((uint32_t)(4 * wave + (lv & 3) + 32 * (lv >> 2)));
+  const uint2 mine = digit_entry((uint32_t)(4 * wave + (lv & 3) + (TH / 16) * (lv >> 2)));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kStores; ++i) {
     const int src = (4 * i + (lane >> 4)) << 2;
     const uint32_t e0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.x);
     const uint32_t e1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mine.y);
-    *reinterpret_cast<uint4 *>(tab + t * 16 + i * kThreads3 * 16) = make_uint4(e0, e1, e0, e1);
+    *reinterpret_cast<uint4 *>(tab + t * 16 + i * TH * 16) = make_uint4(e0, e1, e0, e1);
   }
 }
 
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
 #pragma unroll
   for (int r = 0; r < R; ++r) issue(wr[r], nr[r], r);
 
-  build_digit_table(tab, t);
+  build_digit_table<kThreads3>(tab, t);
   convert(qraw);
   if (CHUNKED) load_codes(qraw, 1);
   __syncthreads();
@@ -332,9 +335,9 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_mma_kernel(T3MmaArgs A) {
 // lane half h takes bytes 14 h .. 14 h + 13, bytes 14 h + 2 s and + 1 in
 // step s.  The int32 group sums are exact (|.| <= 128 * 127), scaled by the
 // row's fp32 norm and added in fp32 once per group, in group order.
-//  * Workgroup tile 64 MB tokens x 128 NB rows: eight waves, two along the
-//    tokens and four along the rows, each 32 MB x 32 NB (MB x NB MFMA
-//    tiles).  Every wave runs all of K.
+//  * Workgroup tile 64 MB tokens x 32 NB WN rows: 2 WN waves, two along the
+//    tokens and WN along the rows, each 32 MB x 32 NB (MB x NB MFMA tiles).
+//    Every wave runs all of K.
 //  * The tokens' codes of one group are staged once per workgroup in LDS,
 //    already laid out as A operands: per token 28 eight-byte slot groups (five
 //    codes, three zeros; the codes past the group's 128 zero), 240 bytes a
@@ -360,12 +363,13 @@ struct T3GemmArgs {
   float cfac;
 };
 
-template <int MB, int NB>
-__global__ __launch_bounds__(kThreads3) void cq_t3_gemm_kernel(T3GemmArgs A) {
-  constexpr int BM = 64 * MB, BN = 128 * NB;
+template <int MB, int NB, int WN>
+__global__ __launch_bounds__(128 * WN) void cq_t3_gemm_kernel(T3GemmArgs A) {
+  constexpr int TH = 128 * WN;
+  constexpr int BM = 64 * MB, BN = 32 * NB * WN;
   constexpr int kABuf = BM * kT3GStride;
   constexpr int kItems = BM * 7;                   // A staging items: 20 codes (4 slot groups) each
-  constexpr int kIt = (kItems + kThreads3 - 1) / kThreads3;
+  constexpr int kIt = (kItems + TH - 1) / TH;
   static_assert(kTab3 + 2 * kABuf <= 163840, "LDS of one CU");
   __shared__ __align__(16) uint8_t lds[kTab3 + 2 * kABuf];
   uint8_t *const tab = lds;
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_gemm_kernel(T3GemmArgs A) {
   bool itail[kIt];
 #pragma unroll
   for (int u = 0; u < kIt; ++u) {
-    const int i = t + u * kThreads3;
+    const int i = t + u * TH;
     const int tl = i / 7, p = i - 7 * (i / 7);
     const bool ok = i < kItems;
     iwhere[u] = ok ? tl * kT3GStride + 32 * p : -1;
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_gemm_kernel(T3GemmArgs A) {
   load_a(0);
   load_b(0, 0);
   load_b(1, 1);
-  build_digit_table(tab, t);
+  build_digit_table<TH>(tab, t);
   stage_a(0);
   load_a(1);
   __syncthreads();
@@ -545,12 +549,12 @@ __global__ __launch_bounds__(kThreads3) void cq_t3_gemm_kernel(T3GemmArgs A) {
     }
 }
 
-template <int MB, int NB>
+template <int MB, int NB, int WN>
 hipError_t launch_t3_gemm_tiles(T3GemmArgs A, hipStream_t s) {
   A.tiles_m = (A.m + 64 * MB - 1) / (64 * MB);
-  A.tiles_n = (A.rows + 128 * NB - 1) / (128 * NB);
+  A.tiles_n = (A.rows + 32 * NB * WN - 1) / (32 * NB * WN);
   const int grid = ((A.tiles_m * A.tiles_n + 7) / 8) * 8;
-  cq_t3_gemm_kernel<MB, NB><<<grid, kThreads3, 0, s>>>(A);
+  cq_t3_gemm_kernel<MB, NB, WN><<<grid, 128 * WN, 0, s>>>(A);
   return hipGetLastError();
 }
 
@@ -625,9 +629,9 @@ hipError_t launch_cq_t3_gemm(const uint8_t *blob, const bqm_cq_layout &L, const 
   A.cfac = T.cscale / (float)kGroup;
   auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((L.rows + bn - 1) / bn); };
   const long want = (long)num_cus * 7 / 8;
-  if (tiles(128, 256) >= want) return launch_t3_gemm_tiles<2, 2>(A, s);
-  if (tiles(128, 128) >= want) return launch_t3_gemm_tiles<2, 1>(A, s);
-  return launch_t3_gemm_tiles<1, 1>(A, s);
+  if (tiles(128, 256) >= want) return launch_t3_gemm_tiles<2, 1, 8>(A, s);
+  if (tiles(128, 128) >= want) return launch_t3_gemm_tiles<2, 1, 4>(A, s);
+  return launch_t3_gemm_tiles<1, 1, 4>(A, s);
 }
 
 }  // namespace bqm
