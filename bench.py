@@ -456,6 +456,30 @@ def bench_q4_0(B, torch, dev, steps, warmup):
 
     cold = graph_repeats_ms(torch, [(lambda k=k: cold_pass(k)) for k in range(ncop)], repeats=3)
     ms_cold = sorted(cold)[1]
+    # stacked: each layer's q, k, v as one [520, 312] matrix and gate, up as
+    # one [2184, 312] (the matrices that read the same activations, stacked
+    # as inference engines do: row-major blocks concatenate): 41 launches of
+    # the same kernels over the same bytes
+    per = len(inputs.MINUEZA_LAYER_SHAPES)
+    stacked = []
+    for base in range(0, len(items) - 1, per):
+        for grp in ((0, 1, 2), (3,), (4, 5), (6,)):
+            its = [items[base + i] for i in grp]
+            rows_s = sum(it[0] for it in its)
+            stacked.append((rows_s, its[0][1], torch.cat([it[2] for it in its]), its[0][3],
+                            torch.empty((1, rows_s), dtype=torch.float32, device=dev)))
+    stacked.append(items[-1])
+    st_copies = [[it[2]] + [it[2].clone() for _ in range(ncop - 1)] for it in stacked]
+    torch.cuda.synchronize()
+
+    def stacked_pass(k):
+        for i, (r_, c_, _, x_, y_) in enumerate(stacked):
+            B.q4_0_gemv(st_copies[i][k], r_, c_, x_, y=y_)
+
+    ms_st = graph_mean_ms(torch, [(lambda: stacked_pass(0)) for _ in range(max(steps, 10))])
+    st_cold = graph_repeats_ms(torch, [(lambda k=k: stacked_pass(k)) for k in range(ncop)], repeats=3)
+    ms_st_cold = sorted(st_cold)[1]
+    del st_copies
     head_pool = copies[-1] + [blocks.clone() for _ in range(max(0, pool_copies(blocks.numel()) - ncop))]
     hc = graph_repeats_ms(torch, [(lambda k=k: B.q4_0_gemv(head_pool[k], rows, cols, x, y=y))
                                   for k in range(len(head_pool))], repeats=3)
@@ -468,7 +492,9 @@ def bench_q4_0(B, torch, dev, steps, warmup):
                 note="us_graph / head_us: weights warm in the Infinity Cache (the 13 MB pass fits); "
                      "*_hbm_cold: cycling >= 1 GiB of copies",
                 pass_us_hbm_cold=ms_cold * 1e3, pass_gbps_hbm_cold=total / ms_cold / 1e6,
-                pass_copies=ncop, head_us_hbm_cold=ms_head_cold * 1e3,
+                pass_copies=ncop, stacked_launches=len(stacked), stacked_us_graph=ms_st * 1e3,
+                stacked_us_hbm_cold=ms_st_cold * 1e3, stacked_gbps_hbm_cold=total / ms_st_cold / 1e6,
+                head_us_hbm_cold=ms_head_cold * 1e3,
                 head_gbps_hbm_cold=blocks.numel() / ms_head_cold / 1e6,
                 head_frac_hbm_cold=blocks.numel() / ms_head_cold / 1e6 / HBM_PEAK_GBPS)
 

@@ -271,6 +271,20 @@ def test_q4_0_gemv_parity(rows, cols, batch):
     P.check_q4_0(y, blk, cols, x, label=f"q4_0_gemv {rows}x{cols} b{batch}")
 
 
+def test_q4_0_stacked_rows_match_separate():
+    """Matrices that read the same activations (a layer's q, k, v; gate and
+    up), stacked row-wise into one launch, give every row bit for bit the
+    result of its own matrix's launch."""
+    rng = np.random.default_rng(1300)
+    for group in (((312, 312), (104, 312), (104, 312)), ((1092, 312), (1092, 312)), ((40, 1092), (300, 1092))):
+        cols = group[0][1]
+        x = dev(inputs.activations(rng, 1, cols))
+        blks = [B.q4_0_pack(dev(inputs.weight_matrix(rng, r, cols))) for r, _ in group]
+        ys = np.concatenate([host(B.q4_0_gemv(b, r, cols, x)) for b, (r, _) in zip(blks, group)], axis=1)
+        yst = host(B.q4_0_gemv(torch.cat(blks), sum(r for r, _ in group), cols, x))
+        assert np.array_equal(ys.view(np.uint32), yst.view(np.uint32)), group
+
+
 # tall matrices of 9..16 blocks a row take the persistent row-tile kernel
 # (16 lanes a row, activations in registers): a full last block ending the
 # buffer (512 cols), ragged ones with cols % 4 != 0 (301, 318: 4-byte
