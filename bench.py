@@ -551,7 +551,8 @@ def bench_q4_0_a8(B, torch, dev, steps, warmup, m=512):
     """The Minueza Q4_0 pass with int8 activations (A8, no rotation): decode
     (one token) and prefill (m tokens), graph-timed; each matrix's input is
     quantized with act_fwht_quant_a8 (group 1) then multiplied.  Times with
-    the A8 launches and for the products alone are both given."""
+    the A8 launches and for the products alone are both given, and for decode
+    the fused entry (one launch a matrix)."""
     from bit_quantized_matmul_amd import inputs
     wl = inputs.minueza_q4_0_pass()
     rng = inputs.rng_for(13)
@@ -580,14 +581,20 @@ def bench_q4_0_a8(B, torch, dev, steps, warmup, m=512):
     def t(fn):
         return sorted(graph_repeats_ms(torch, [fn] * max(steps, 5), repeats=5))[2]
 
-    d_a8, d_prod = t(one(dec, False, True)), t(one(dec, False, False))
+    def fused():
+        for rows, cols, blocks, x, q, s, y in dec:
+            B.q4_0_gemv_a8_f32(blocks, rows, cols, x, y=y)
+
+    d_a8, d_prod, d_fused = t(one(dec, False, True)), t(one(dec, False, False)), t(fused)
     p_a8, p_prod = t(one(pre, True, True)), t(one(pre, True, False))
     rows, cols, blocks, x, q, s, y = pre[-1]
     head = sorted(graph_repeats_ms(torch, [lambda: B.q4_0_gemm_a8(blocks, rows, cols, q, s, y=y)] * 8))[2]
     head_tops = 2 * m * rows * cols / head / 1e9
     return dict(
         decode=dict(launches=2 * len(dec), bytes=total, us_with_a8=d_a8 * 1e3, us_products_only=d_prod * 1e3,
-                    gbps_products_only=total / d_prod / 1e6, note="weights warm in the Infinity Cache"),
+                    gbps_products_only=total / d_prod / 1e6, us_fused=d_fused * 1e3, fused_launches=len(dec),
+                    note="weights warm in the Infinity Cache; us_fused: q4_0_gemv_a8_f32, the codes formed "
+                         "in each product's launch"),
         prefill=dict(tokens=m, gop=flops / 1e9, us_with_a8=p_a8 * 1e3, us_products_only=p_prod * 1e3,
                      tops_products_only=flops / p_prod / 1e9,
                      frac_int8_peak=flops / p_prod / 1e9 / INT8_MFMA_PEAK_TOPS,

@@ -23,7 +23,7 @@ EXPORTED = (
     "cq_pack_info", "cq_analytic_levels", "act_fwht_quant_a8", "cq_gemv", "cq_gemv_f32",
     "cq_gemm", "q4_0_gemv", "q4_0_gemm", "cq_pack", "q4_0_pack", "cq_codebook_fit", "bqm_strerror",
     "kmcu_header", "kmcu_tensor", "kmcu_find", "kmcu_upload", "kmcu_upload_data", "cq_gemv_f32_noalloc",
-    "q4_0_gemv_a8", "q4_0_gemm_a8", "cq_gemv_lut",
+    "q4_0_gemv_a8", "q4_0_gemm_a8", "cq_gemv_lut", "q4_0_gemv_a8_f32",
 )
 KMCU_F32, KMCU_Q4 = 1, 2
 
@@ -98,6 +98,7 @@ def load_library() -> ctypes.CDLL:
         "q4_0_gemm": ([P, I, I, P, I, P, P], I),
         "q4_0_gemv_a8": ([P, I, I, P, P, I, P, P], I),
         "q4_0_gemm_a8": ([P, I, I, P, P, I, P, P], I),
+        "q4_0_gemv_a8_f32": ([P, I, I, P, I, P, P, P, P], I),
         "cq_pack": ([P, LP, F, P, P, P], I),
         "q4_0_pack": ([P, I, I, P, P], I),
         "cq_codebook_fit": ([P, I64, I, I, P, P, P], I),
@@ -351,6 +352,30 @@ def q4_0_gemv_a8(blocks, rows: int, cols: int, q, scale, y=None):
 def q4_0_gemm_a8(blocks, rows: int, cols: int, q, scale, y=None):
     """Q4_0 blocks x int8 codes q [m, cols] -> fp32 y [m, rows] on the int8 matrix cores."""
     return _q4_0_a8("q4_0_gemm_a8", blocks, rows, cols, q, scale, y)
+
+
+def q4_0_gemv_a8_f32(blocks, rows: int, cols: int, x, y=None, q_out=None, scale_out=None):
+    """Q4_0 blocks x fp32 x [batch, cols], quantized per token to int8 in the
+    same launch (act_fwht_quant_a8, group 1) -> fp32 y [batch, rows];
+    q_out [batch, cols] int8 and scale_out [batch] receive the codes and
+    scales when given."""
+    torch = _torch()
+    batch = _rows2d(x, cols, "x")
+    _at_least(blocks, q4_0_nbytes(rows, cols), "blocks")
+    if y is None:
+        y = torch.empty((batch, rows), dtype=torch.float32, device=x.device)
+    _shape(y, (batch, rows), "y")
+    qp = sp = None
+    if q_out is not None:
+        _shape(q_out, (batch, cols), "q_out")
+        qp = _dev(q_out, torch.int8, "q_out")
+    if scale_out is not None:
+        _shape(scale_out, (batch,), "scale_out")
+        sp = _dev(scale_out, torch.float32, "scale_out")
+    _check("q4_0_gemv_a8_f32", load_library().q4_0_gemv_a8_f32(
+        _dev(blocks, torch.uint8, "blocks"), rows, cols, _dev(x, torch.float32, "x"), batch,
+        _dev(y, torch.float32, "y"), qp, sp, _stream()))
+    return y
 
 
 # ---------------------------------------------------------------- KMCU container

@@ -405,6 +405,22 @@ int q4_0_gemv_a8(const void *blocks, int rows, int cols, const int8_t *q, const 
   return status_of(launch_q4_0_gemv_a8((const uint8_t *)blocks, rows, cols, q, scale, batch, y, (hipStream_t)stream));
 }
 
+int q4_0_gemv_a8_f32(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
+                     int8_t *q_out, float *scale_out, bqm_stream_t stream) {
+  if (!blocks || !x || !y || rows < 1 || cols < 1 || batch < 1) return BQM_EINVAL;
+  // 32-bit offsets for the blocks; one token's codes must fit a workgroup's LDS
+  if (batch > 16 || (int64_t)rows * (((int64_t)cols + 31) / 32) * 18 >= ((int64_t)1 << 31) ||
+      !q4_0_gemv_a8_fused_supported(cols, batch))
+    return BQM_ENOTSUP;
+  if (!aligned16(blocks) || ((uintptr_t)x & 3u) || ((uintptr_t)y & 3u) || ((uintptr_t)scale_out & 3u))
+    return BQM_EALIGN;
+  int cus;
+  const int rc = current_device(&cus);
+  if (rc) return rc;
+  return status_of(launch_q4_0_gemv_a8_fused((const uint8_t *)blocks, rows, cols, x, batch, y, q_out, scale_out,
+                                             cus, (hipStream_t)stream));
+}
+
 int q4_0_gemm_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int m, float *y,
                  bqm_stream_t stream) {
   if (!blocks || !q || !scale || !y || rows < 1 || cols < 1 || m < 1) return BQM_EINVAL;

@@ -110,6 +110,11 @@ hipError_t launch_act_quant_a8_unrotated(const float *x, int m, int k, int8_t *q
                                          hipStream_t s);
 hipError_t launch_q4_0_gemv_a8(const uint8_t *blocks, int rows, int cols, const int8_t *q,
                                const float *scale, int batch, float *y, hipStream_t s);
+// Q4_0 A8 GEMV on fp32 activations, codes formed in the launch (batch <= 16;
+// the supported predicate bounds the codes one workgroup holds in LDS).
+bool q4_0_gemv_a8_fused_supported(int cols, int batch);
+hipError_t launch_q4_0_gemv_a8_fused(const uint8_t *blocks, int rows, int cols, const float *x, int batch,
+                                     float *y, int8_t *q_out, float *scale_out, int num_cus, hipStream_t s);
 hipError_t launch_q4_0_gemm_a8(const uint8_t *blocks, int rows, int cols, const int8_t *q, const float *scale,
                                int m, float *y, int num_cus, hipStream_t s);
 hipError_t launch_cq_gemv(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,

@@ -166,6 +166,206 @@ hipError_t gemv_batch(const uint8_t *blocks, int rows, int cols, int nblk, uint3
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ fused GEMV
+//
+// The same GEMV on fp32 activations, their int8 codes formed in the launch
+// with act_fwht_quant_a8's group-1 arithmetic: s = RN(amax / 127) (1 for a
+// zero token), q = clamp(rint(RN(x / s)), -127, 127).  Every workgroup forms
+// all codes of its tokens once, straight into LDS in the staged layout of the
+// kernel above (evens and odds of each 8 codes, each block's code sum), then
+// runs its rows with no further staging: workgroups loop over row passes.  The
+// first pass's blocks are requested first, so their latency overlaps the
+// activations'.
+// rint(x * rcp(s)) decides a code unless x * rcp(s) lies within 1e-4 of a
+// half-integer (its error is below 127 * 2^-22); then RN(x / s) decides it.
+constexpr int kA8FusedMaxLds = 60 * 1024;        // codes of the launch's tokens, per workgroup
+
+template <int BATCH, int P>
+__global__ __launch_bounds__(kA8Threads) void q4_0_gemv_a8_fused_kernel(
+    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t total,
+    const float *__restrict__ x, float *__restrict__ y, int8_t *__restrict__ q_out,
+    float *__restrict__ scale_out) {
+  // x, y, q_out and scale_out start at the launch's first token
+  constexpr int RPW = kA8Threads / P;
+  extern __shared__ __align__(16) uint32_t dyn[];
+  uint32_t *const xs = dyn;                                         // [BATCH][nblk][8]
+  int *const xsum = reinterpret_cast<int *>(dyn + BATCH * nblk * 8);   // [BATCH][nblk]
+  __shared__ float red[BATCH][kA8Threads / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const __amdgpu_buffer_rsrc_t rx = q4_rsrc(x, (uint32_t)(BATCH * cols) * 4u);
+  const __amdgpu_buffer_rsrc_t rw = q4_rsrc(blocks, total);
+  const int j = t % P;
+  // the first row pass's first blocks are requested before anything else, so
+  // their latency overlaps the activations' and the codes'
+  BlockLoad L0;
+  {
+    const int row = blockIdx.x * RPW + t / P;
+    const bool ok = row < rows && j < nblk;
+    L0 = load_block(rw, ok, ok ? (uint32_t)(((size_t)row * nblk + j) * kQ4BlockBytes) : 0u, total);
+  }
+
+  // item i: token i / (4 nblk), block (i / 4) % nblk, codes 8 w .. 8 w + 7 of it
+  // (w = i % 4; the four of a block are one lane quad); columns >= cols read 0
+  const int nitems = BATCH * nblk * 4;
+  auto load_item = [&](int i, float (&v)[8]) {
+    const int w = i & 3, bb = i >> 2;
+    const int b = bb / nblk, c0 = kQ4Block * (bb - b * nblk) + 8 * w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rx, c0 + e < cols ? (uint32_t)(b * cols + c0 + e) * 4u : kQ4OOB, 0, 0));
+  };
+
+  // 1. the tokens' scales, from one pass over the items (a thread's first item
+  // stays in registers for step 2)
+  float keep[8];
+  float m[BATCH];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) m[b] = 0.0f;
+  for (int i = t; i < nitems; i += kA8Threads) {
+    float v[8];
+    load_item(i, v);
+    const int b = (i >> 2) / nblk;
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+    for (int bt = 0; bt < BATCH; ++bt) m[bt] = bt == b ? fmaxf(m[bt], a) : m[bt];
+    if (i == t) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keep[e] = v[e];
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    float mb = m[b];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+    if (lane == 0) red[b][wave] = mb;
+  }
+  __syncthreads();
+  // every thread forms the scales itself (no second barrier)
+  float sc[BATCH];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    float mm = red[b][0];
+#pragma unroll
+    for (int w = 1; w < kA8Threads / 64; ++w) mm = fmaxf(mm, red[b][w]);
+    sc[b] = mm > 0.0f ? __fdiv_rn(mm, 127.0f) : 1.0f;
+  }
+  if (scale_out && blockIdx.x == 0 && t < BATCH) {
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (t == b) scale_out[b] = sc[b];
+  }
+
+  // 2. the codes, in the staged layout
+  for (int i = t; i < nitems; i += kA8Threads) {       // whole quads share a trip count
+    const int w = i & 3, bb = i >> 2;
+    const int b = bb / nblk, blk = bb - b * nblk;
+    float v[8];
+    if (i == t) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = keep[e];
+    } else {
+      load_item(i, v);
+    }
+    float s = sc[0];
+#pragma unroll
+    for (int bt = 1; bt < BATCH; ++bt) s = b == bt ? sc[bt] : s;
+    const float inv = __builtin_amdgcn_rcpf(s);
+    const int c0 = kQ4Block * blk + 8 * w;
+    int c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float r = rintf(v[e] * inv);
+      if (fabsf(fmaf(v[e], inv, -r)) > 0.4999f) r = rintf(__fdiv_rn(v[e], s));
+      c[e] = (int)__builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
+      if (q_out && blockIdx.x == 0 && c0 + e < cols) q_out[(size_t)b * cols + c0 + e] = (int8_t)c[e];
+    }
+    // evens (codes 0, 2, 4, 6) and odds, one byte each
+    const uint32_t e01 = __builtin_amdgcn_perm((uint32_t)c[2], (uint32_t)c[0], 0x0C0C0400u);
+    const uint32_t e23 = __builtin_amdgcn_perm((uint32_t)c[6], (uint32_t)c[4], 0x0C0C0400u);
+    const uint32_t o01 = __builtin_amdgcn_perm((uint32_t)c[3], (uint32_t)c[1], 0x0C0C0400u);
+    const uint32_t o23 = __builtin_amdgcn_perm((uint32_t)c[7], (uint32_t)c[5], 0x0C0C0400u);
+    const uint32_t ev = __builtin_amdgcn_perm(e23, e01, 0x05040100u);
+    const uint32_t od = __builtin_amdgcn_perm(o23, o01, 0x05040100u);
+    *reinterpret_cast<uint2 *>(&xs[(b * nblk + blk) * 8 + 2 * w]) = make_uint2(ev, od);
+    int sum = __builtin_amdgcn_sdot4((int)ev, 0x01010101, 0, false);
+    sum = __builtin_amdgcn_sdot4((int)od, 0x01010101, sum, false);
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (w == 0) xsum[b * nblk + blk] = sum;
+  }
+  __syncthreads();
+
+  // 3. rows: P lanes a row, RPW rows a pass, the workgroups taking the passes in turn
+  bool first = true;
+  for (int r0 = blockIdx.x * RPW; r0 < rows; r0 += gridDim.x * RPW) {
+    const int row = r0 + t / P;
+    const bool rok = row < rows;
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) acc[b] = 0.0f;
+    for (int c0 = 0; c0 < nblk; c0 += P) {
+      const int blk = c0 + j;
+      const bool ok = rok && blk < nblk;
+      BlockLoad L;
+      if (first) {
+        L = L0;
+        first = false;
+      } else {
+        L = load_block(rw, ok, ok ? (uint32_t)(((size_t)row * nblk + blk) * kQ4BlockBytes) : 0u, total);
+      }
+      uint32_t nib[4];
+      const float d = block_fields(L, nib);          // 0 for a lane without a block
+      const int bk = blk < nblk ? blk : 0;
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(&xs[(b * nblk + bk) * 8]);
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(&xs[(b * nblk + bk) * 8 + 4]);
+        const uint32_t xe[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        int isum = -8 * xsum[b * nblk + bk];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          isum = __builtin_amdgcn_sdot4((int)(nib[w] & 0x0F0F0F0Fu), (int)xe[2 * w], isum, false);
+          isum = __builtin_amdgcn_sdot4((int)((nib[w] >> 4) & 0x0F0F0F0Fu), (int)xe[2 * w + 1], isum, false);
+        }
+        acc[b] = fmaf(d, (float)isum, acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+      for (int o = P / 2; o >= 1; o >>= 1) acc[b] += __shfl_xor(acc[b], o, P);
+    if (rok && j == 0) {
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) y[(size_t)b * rows + row] = acc[b] * sc[b];
+    }
+  }
+}
+
+template <int BATCH>
+hipError_t gemv_fused_batch(const uint8_t *blocks, int rows, int cols, int nblk, uint32_t total, const float *x,
+                            float *y, int8_t *q_out, float *scale_out, int num_cus, hipStream_t s) {
+  int P = 4;
+  while (P < 64 && P < nblk) P *= 2;               // as the staged kernel: the same sums, bit for bit
+  const int passes = (rows + kA8Threads / P - 1) / (kA8Threads / P);
+  const int grid = passes < 2 * num_cus ? passes : 2 * num_cus;
+  const size_t lds = (size_t)BATCH * nblk * 36;
+  switch (P) {
+#define BQM_A8F_CASE(PP)                                                                                 \
+  case PP:                                                                                               \
+    q4_0_gemv_a8_fused_kernel<BATCH, PP><<<grid, kA8Threads, lds, s>>>(blocks, rows, cols, nblk, total, x, \
+                                                                       y, q_out, scale_out);           \
+    break;
+    BQM_A8F_CASE(4) BQM_A8F_CASE(8) BQM_A8F_CASE(16) BQM_A8F_CASE(32) BQM_A8F_CASE(64)
+#undef BQM_A8F_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- GEMM
 
 constexpr int kA8TileM = 64, kA8TileN = 64;       // tokens x weight rows per workgroup (KSPLIT 1)
@@ -302,6 +502,38 @@ hipError_t launch_q4_0_gemv_a8(const uint8_t *blocks, int rows, int cols, const 
                              : gemv_batch<2, false>(blocks, rows, cols, nblk, tb, q, qbytes, b0, sb, yb, s);
     else e = al ? gemv_batch<1, true>(blocks, rows, cols, nblk, tb, q, qbytes, b0, sb, yb, s)
                 : gemv_batch<1, false>(blocks, rows, cols, nblk, tb, q, qbytes, b0, sb, yb, s);
+    if (e != hipSuccess) return e;
+    b0 += nb;
+  }
+  return hipSuccess;
+}
+
+// tokens a launch: 4, 2 or 1, as many as the remaining batch and the LDS allow
+static int fused_slice(int remaining, int nblk) {
+  for (int nb = 4; nb > 1; nb >>= 1)
+    if (remaining >= nb && (size_t)nb * nblk * 36 <= (size_t)kA8FusedMaxLds) return nb;
+  return 1;
+}
+
+bool q4_0_gemv_a8_fused_supported(int cols, int batch) {
+  const size_t nblk = ((size_t)cols + kQ4Block - 1) / kQ4Block;
+  return (size_t)batch * cols < ((size_t)1 << 29) && nblk * 36 <= (size_t)kA8FusedMaxLds;
+}
+
+hipError_t launch_q4_0_gemv_a8_fused(const uint8_t *blocks, int rows, int cols, const float *x, int batch,
+                                     float *y, int8_t *q_out, float *scale_out, int num_cus, hipStream_t s) {
+  const int nblk = (cols + kQ4Block - 1) / kQ4Block;
+  const uint32_t total = (uint32_t)((size_t)rows * nblk * kQ4BlockBytes);
+  for (int b0 = 0; b0 < batch;) {
+    const int nb = fused_slice(batch - b0, nblk);
+    const float *xb = x + (size_t)b0 * cols;
+    float *yb = y + (size_t)b0 * rows;
+    int8_t *qb = q_out ? q_out + (size_t)b0 * cols : nullptr;
+    float *sb = scale_out ? scale_out + b0 : nullptr;
+    hipError_t e;
+    if (nb == 4) e = gemv_fused_batch<4>(blocks, rows, cols, nblk, total, xb, yb, qb, sb, num_cus, s);
+    else if (nb == 2) e = gemv_fused_batch<2>(blocks, rows, cols, nblk, total, xb, yb, qb, sb, num_cus, s);
+    else e = gemv_fused_batch<1>(blocks, rows, cols, nblk, total, xb, yb, qb, sb, num_cus, s);
     if (e != hipSuccess) return e;
     b0 += nb;
   }

@@ -253,6 +253,21 @@ int q4_0_gemv_a8(const void *blocks, int rows, int cols, const int8_t *q, const 
 int q4_0_gemm_a8(const void *blocks, int rows, int cols, const int8_t *q, const float *scale, int m,
                  float *y, bqm_stream_t stream);
 
+/* q4_0_gemv_a8 on fp32 activations, their codes formed in the same launch:
+ * the per-token codes and scale of act_fwht_quant_a8 with group 1 (8-bit
+ * activations, Needle article, section 1; s = RN(amax / 127), 1 for a zero
+ * token; q = clamp(rint(RN(x / s)), -127, 127)), then the q4_0_gemv_a8 sum,
+ * so y, q_out and scale_out equal the two-launch path's bit for bit.
+ * blocks [device] as for q4_0_gemv (16-byte aligned); x [device] fp32
+ * [batch, cols] (4-byte aligned); y [device] fp32 [batch, rows]; q_out
+ * [device] int8 [batch, cols] and scale_out [device] fp32 [batch] receive
+ * the codes and scales when non-NULL.  1 <= batch <= 16.  Every workgroup
+ * holds the codes of up to 4 tokens in LDS (36 bytes a token and block):
+ * BQM_ENOTSUP past 1706 blocks a row (cols > 54592), when the blocks reach
+ * 2^31 bytes, or batch > 16. */
+int q4_0_gemv_a8_f32(const void *blocks, int rows, int cols, const float *x, int batch, float *y,
+                     int8_t *q_out, float *scale_out, bqm_stream_t stream);
+
 /* Encode fp32 weights into a CQ blob on the device (Needle article,
  * section 1: group FWHT with the normalized Walsh-Hadamard matrix, nearest
  * Lloyd-Max level per coordinate, fp16 group L2 norm, LSB-first packing).

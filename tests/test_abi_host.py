@@ -137,6 +137,17 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
         assert fn(p, 1 << 27, 32, p, p, 1, p, None) == E.BQM_ENOTSUP          # blocks past 2^31 bytes
     assert lib.q4_0_gemv_a8(p, 4, 312, p, p, 17, p, None) == E.BQM_ENOTSUP
     assert lib.q4_0_gemm_a8(p, 4, 1 << 20, p, p, 4096, p, None) == E.BQM_ENOTSUP   # codes past 2^31 bytes
+    # the fused A8 Q4_0 GEMV: fp32 activations, codes of one token within a workgroup's LDS
+    f = lib.q4_0_gemv_a8_f32
+    assert f(None, 4, 312, p, 1, p, None, None, None) == E.BQM_EINVAL
+    assert f(p, 4, 312, p, 0, p, None, None, None) == E.BQM_EINVAL
+    assert f(p, 4, 0, p, 1, p, None, None, None) == E.BQM_EINVAL
+    assert f(p, 4, 312, p, 17, p, None, None, None) == E.BQM_ENOTSUP
+    assert f(p, 4, 54593, p, 1, p, None, None, None) == E.BQM_ENOTSUP            # 1707 blocks a row
+    assert f(p, 1 << 27, 32, p, 1, p, None, None, None) == E.BQM_ENOTSUP         # blocks past 2^31 bytes
+    assert f(ctypes.c_void_p(4100), 4, 312, p, 1, p, None, None, None) == E.BQM_EALIGN
+    assert f(p, 4, 312, ctypes.c_void_p(4098), 1, p, None, None, None) == E.BQM_EALIGN
+    assert f(p, 4, 312, p, 1, p, None, ctypes.c_void_p(4098), None) == E.BQM_EALIGN
     # the lookup-table GEMV: binary and ternary only, widths its LDS tables hold
     assert lib.cq_gemv_lut(p, ctypes.byref(lay), p, p, 1, p, None) == E.BQM_ENOTSUP       # 4-bit
     b1 = binding.cq_pack_info(64, 8192, 128, 1)

@@ -100,6 +100,51 @@ def test_q4_0_a8_mixed_scale_rows(entry, rows, cols, n):
     check(y, blk, cols, q, s, f"mixed q4_0_{entry}_a8 {rows}x{cols} n{n}")
 
 
+# the fused entry (codes formed in the launch): token slices of 4, 2 and 1,
+# widths of 1..1706 blocks (ragged, cols % 4 != 0), a zero token, rows from 1
+# to the tied head; y, the codes and the scales equal the two-launch path's
+# bit for bit, and y the oracle's within the bound
+@pytest.mark.parametrize("rows,cols,batch", [(312, 312, 1), (104, 312, 3), (1092, 312, 16), (312, 1092, 7),
+                                             (5, 33, 2), (1, 1, 1), (32002, 312, 1), (64, 14336, 5),
+                                             (40, 54592, 1), (257, 101, 4), (33, 4097, 6)])
+def test_q4_0_gemv_a8_f32_matches_two_launches(rows, cols, batch):
+    rng = np.random.default_rng(1650 + rows + cols + batch)
+    w = inputs.weight_matrix(rng, rows, cols)
+    x = inputs.activations(rng, batch, cols)
+    if batch > 1:
+        x[1] = 0.0                                        # zero token: s = 1, q = 0, y = 0
+    blk = oq4.encode(w)
+    db, dx = dev(blk.ravel()), dev(x)
+    q_out = torch.empty((batch, cols), dtype=torch.int8, device=DEV)
+    s_out = torch.empty((batch,), dtype=torch.float32, device=DEV)
+    y = host(B.q4_0_gemv_a8_f32(db, rows, cols, dx, q_out=q_out, scale_out=s_out))
+    q, s = B.act_fwht_quant_a8(dx, group=1)
+    y2 = host(B.q4_0_gemv_a8(db, rows, cols, q, s))
+    assert np.array_equal(host(q_out), host(q))
+    assert np.array_equal(host(s_out).view(np.uint32), host(s).view(np.uint32))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    q_ref, s_ref = oa8.act_quant_a8_unrotated(x, "fp32")
+    assert np.array_equal(host(q_out), q_ref)
+    if batch > 1:
+        assert np.all(y[1] == 0.0)
+    sel = np.arange(rows) if rows <= 2048 else np.sort(rng.choice(rows, 64, replace=False))
+    check(y[:, sel], blk[sel], cols, q_ref, s_ref, f"q4_0_gemv_a8_f32 {rows}x{cols} b{batch}")
+
+
+def test_q4_0_gemv_a8_f32_ties():
+    """Quotients that are exact halves take the correctly rounded division's
+    tie rule (the codes of the hand-worked tie row), in the fused launch."""
+    g = {r[0].split(":", 1)[0]: r[0].split(":", 1)[1].strip() for r in read_golden_rows("a8_ties.txt")}
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0] = _sparse(g["row0_u"]).astype(np.float32)
+    rng = np.random.default_rng(1660)
+    blk = oq4.encode(inputs.weight_matrix(rng, 40, 128))
+    q_out = torch.empty((1, 128), dtype=torch.int8, device=DEV)
+    B.q4_0_gemv_a8_f32(dev(blk.ravel()), 40, 128, dev(x), q_out=q_out)
+    q_ref, _ = oa8.act_quant_a8_unrotated(x, "fp32")
+    assert np.array_equal(host(q_out), q_ref)
+
+
 def test_q4_0_a8_device_codes_end_to_end():
     """Device A8 codes feed the device products: the whole int8 path on the
     Minueza head shape at 64 tokens against the oracle's codes and product."""
