@@ -441,8 +441,18 @@ def bench_q4_0(B, torch, dev, steps, warmup):
     ms_eager = t.stop_ms() / steps
     # the tied head alone (the only matrix large enough to be bandwidth-bound),
     # graph-timed: eager launches from Python are host-bound at this size
+    # each distinct matrix shape alone (the first layer's matrices), graph-timed, warm
+    per_matrix = {}
+    for (label, w), it in zip(wl.weights[:len(inputs.MINUEZA_LAYER_SHAPES)], items):
+        r_, c_, b_, x_, y_ = it
+        key = f"{r_}x{c_}"
+        if key in per_matrix:
+            continue
+        ms_m = graph_mean_ms(torch, [(lambda: B.q4_0_gemv(b_, r_, c_, x_, y=y_)) for _ in range(max(steps, 20))])
+        per_matrix[key] = dict(us=ms_m * 1e3, gbps=b_.numel() / ms_m / 1e6)
     rows, cols, blocks, x, y = items[-1]
     ms_head = graph_mean_ms(torch, [(lambda: B.q4_0_gemv(blocks, rows, cols, x, y=y)) for _ in range(max(steps, 20))])
+    per_matrix[f"{rows}x{cols}"] = dict(us=ms_head * 1e3, gbps=blocks.numel() / ms_head / 1e6)
     # HBM-cold: >= 1 GiB of distinct copies of the whole pass, one graph of
     # consecutive passes each on the next copy (the 256 MB Infinity Cache
     # cannot hold them); the head alone likewise over its own pool
@@ -487,6 +497,7 @@ def bench_q4_0(B, torch, dev, steps, warmup):
     del copies, head_pool
     torch.cuda.synchronize()
     return dict(launches=len(items), bytes=total, us_graph=ms * 1e3, gbps_graph=total / ms / 1e6,
+                per_matrix_warm=per_matrix,
                 us_eager=ms_eager * 1e3, head_us=ms_head * 1e3,
                 head_gbps=blocks.numel() / ms_head / 1e6,
                 note="us_graph / head_us: weights warm in the Infinity Cache (the 13 MB pass fits); "
