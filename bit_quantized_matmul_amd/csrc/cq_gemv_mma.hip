@@ -197,8 +197,11 @@ struct MmaArgs {
 // blocks of 16 rows per workgroup; CHUNKED: more than one chunk, the tiles
 // (chunk, row block) then run in a loop whose weight loads run two tiles
 // ahead across chunk ends, the next chunk's codes one chunk ahead, and the
-// row blocks' partial sums gather in LDS.
-template <int IB, int PD, int NRB, bool CHUNKED>
+// row blocks' partial sums gather in LDS.  KS = 2: workgroups 2 j and 2 j + 1
+// take the two halves of K of the same row blocks, each reading only its
+// half's codes, and add their results into y, which the caller has zeroed:
+// two addends onto zero give the same sum in either order.
+template <int IB, int PD, int NRB, bool CHUNKED, int KS>
 __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, LevelTable T) {
   // one array, the table at its start: table addresses need no base added
   __shared__ __align__(16) uint8_t lds[kTabBytes + kRedBytes];
@@ -207,18 +210,21 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // the eighth of each chunk
   const int K = A.cols, N = A.rows, ng = K / kGroup;
-  const int nck = CHUNKED ? (ng + kChunkGroups - 1) / kChunkGroups : 1;
+  const int kh = KS == 1 ? 0 : (int)blockIdx.x % KS;           // this workgroup's part of K
+  const int rg = KS == 1 ? (int)blockIdx.x : (int)blockIdx.x / KS;
+  const int gb = kh * ng / KS, ge = (kh + 1) * ng / KS;       // its groups gb .. ge - 1
+  const int nck = CHUNKED ? (ge - gb + kChunkGroups - 1) / kChunkGroups : 1;
   const int ntiles = nck * NRB;
   const int row_bytes = K * IB / 8;
   const int h = lane >> 4, l16 = lane & 15;
-  const int rb0 = blockIdx.x * NRB;
+  const int rb0 = rg * NRB;
   const __amdgpu_buffer_rsrc_t ridx = rsrc(A.idx, A.idx_bytes);
   const __amdgpu_buffer_rsrc_t rnrm = rsrc(A.norms, A.norm_bytes);
   const __amdgpu_buffer_rsrc_t rq = rsrc(A.q, (uint32_t)(A.batch * K));
   // the wave's groups of chunk c: g0 .. g0 + ngw - 1 (ngw <= PD)
   auto eighth = [&](int c, int &g0, int &ngw) {
-    const int base = c * kChunkGroups;
-    const int ngc = ng - base < kChunkGroups ? ng - base : kChunkGroups;
+    const int base = gb + c * kChunkGroups;
+    const int ngc = ge - base < kChunkGroups ? ge - base : kChunkGroups;
     g0 = base + wave * ngc / kWaves;
     ngw = base + (wave + 1) * ngc / kWaves - g0;
   };
@@ -373,9 +379,17 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
     float v = 0.0f;
 #pragma unroll
     for (int w8 = 0; w8 < kWaves; ++w8) v += red[((w8 * NRB + i) * 4 + r) * 64 + ln];
-    const int row = blockIdx.x * wrows + rr;
-    if (tk < A.batch && row < N) A.y[(size_t)tk * N + row] = v * (A.scale[tk] * cfac);
+    const int row = rg * wrows + rr;
+    if (tk < A.batch && row < N) {
+      if constexpr (KS == 1) A.y[(size_t)tk * N + row] = v * (A.scale[tk] * cfac);
+      else atomicAdd(&A.y[(size_t)tk * N + row], v * (A.scale[tk] * cfac));
+    }
   }
+}
+
+__global__ void zero_f32_kernel(float *__restrict__ y, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = 0.0f;
 }
 
 }  // namespace
@@ -395,8 +409,20 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
   // count rounded up to a power of two
   const int rb_total = (L.rows + 15) / 16;
   const int per_cu = (rb_total + num_cus - 1) / num_cus;
-  const int nrb = per_cu <= 1 ? 1 : per_cu <= 2 ? 2 : per_cu <= 4 ? 4 : kRBMax;
-  const int grid = (rb_total + nrb - 1) / nrb;
+  const int ng = L.cols / kGroup, pd_need = (ng + kWaves - 1) / kWaves;
+  // one row block a CU, long rows and more than 8 tokens (the codes a
+  // workgroup reads then outweigh its weights): split K in two (each
+  // workgroup two row blocks, half the codes), the halves added into y after
+  // a zero fill (the fill's launch costs as much as the split saves at 4 tokens)
+  const bool split = per_cu <= 1 && ng >= 2 * kChunkGroups && rb_total >= 2 && batch > 8;
+  const int nrb = split ? 2 : per_cu <= 1 ? 1 : per_cu <= 2 ? 2 : per_cu <= 4 ? 4 : kRBMax;
+  const int grid = (rb_total + nrb - 1) / nrb * (split ? 2 : 1);
+  if (split) {
+    const int n = batch * L.rows;
+    zero_f32_kernel<<<(n + 255) / 256, 256, 0, s>>>(y, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   MmaArgs A{};
   A.idx = blob;
   A.norms = reinterpret_cast<const uint16_t *>(blob + L.norms_offset);
@@ -408,15 +434,18 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
   A.batch = batch;
   A.idx_bytes = (uint32_t)L.idx_bytes;
   A.norm_bytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);
-  const int ng = L.cols / kGroup, pd_need = (ng + kWaves - 1) / kWaves;
   auto with_nrb = [&](auto ib, auto pd, auto chunked) -> hipError_t {
     constexpr int IB = decltype(ib)::value, PD = decltype(pd)::value;
     constexpr bool CH = decltype(chunked)::value;
+    if (CH && split) {
+      cq_gemv_mma_kernel<IB, PD, 2, CH, 2><<<grid, kThreadsV, 0, s>>>(A, T);
+      return hipGetLastError();
+    }
     switch (nrb) {
-      case 1: cq_gemv_mma_kernel<IB, PD, 1, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 2: cq_gemv_mma_kernel<IB, PD, 2, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 4: cq_gemv_mma_kernel<IB, PD, 4, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      default: cq_gemv_mma_kernel<IB, PD, kRBMax, CH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 1: cq_gemv_mma_kernel<IB, PD, 1, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 2: cq_gemv_mma_kernel<IB, PD, 2, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 4: cq_gemv_mma_kernel<IB, PD, 4, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      default: cq_gemv_mma_kernel<IB, PD, kRBMax, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
     }
     return hipGetLastError();
   };

@@ -116,7 +116,11 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * (>= 3 when cols > 4096) and cols <= 16384 the product runs on the matrix
  * cores in one pass over the weights for all tokens: exact fp16 levels x
  * exact fp16 codes, fp32 accumulation per group, fp32 norm per group, the
- * groups summed in a fixed order.  Batch 1 and 2 otherwise run on the VALU
+ * groups summed in a fixed order.  With more than 8 tokens, at most 16 rows
+ * a CU and at least 64 groups a row, the call is two launches: y is zeroed,
+ * then two halves of K are summed as above and each half's scaled result is
+ * added into y atomically (two addends onto zero: the same bits in either
+ * order, so results stay deterministic).  Batch 1 and 2 otherwise run on the VALU
  * GEMV; for cols > 16384 batch > 4 runs on the cq_gemm kernel with that
  * kernel's arithmetic and bound (level x norm x 2^e_n rounded to fp16 once
  * per weight, see cq_gemm) and smaller batches on the VALU GEMV, 4 tokens per

@@ -155,11 +155,18 @@ def oracle_case(rng, rows, cols, code, batch, codebooks):
                                              # columns K in chunks (5120 x 8, x 3) and the
                                              # VALU GEMV for 2 tokens (5120 x 2); past 16384
                                              # columns more than 4 tokens take the GEMM
-                                             # kernel (20480 x 5, 36864 x 8)
+                                             # kernel (20480 x 5, 36864 x 8); one row block
+                                             # a CU, 64+ groups a row and more than 8
+                                             # tokens split K in two halves (8192: one chunk
+                                             # each; 8320: 32 and 33 groups, 3 row blocks;
+                                             # 12288; 16384 with 2 row blocks; 8192 at 6
+                                             # tokens: no split)
                                              (77, 128, 9), (1000, 384, 5), (300, 4096, 12),
                                              (5000, 512, 6), (9000, 256, 16), (40000, 128, 7),
                                              (40, 5120, 8), (40, 5120, 3), (40, 5120, 2),
-                                             (20, 20480, 5), (9, 36864, 8)])
+                                             (20, 20480, 5), (9, 36864, 8),
+                                             (300, 8192, 10), (33, 8320, 9), (1000, 12288, 16), (17, 16384, 12),
+                                             (300, 8192, 6)])
 def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
     rng = np.random.default_rng(400 + code * 7 + rows + batch)
     lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, batch, codebooks)
@@ -410,6 +417,12 @@ def test_results_are_deterministic(codebooks):
     d = host(B.cq_gemm(db, lay, codebooks[4], dq, ds))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert np.array_equal(c.view(np.uint32), d.view(np.uint32))
+    # the K-split batched GEMV (two halves added into y): the same bits every run
+    lv, idx, n16, blob, q, s = oracle_case(rng, 300, 8192, 4, 12, codebooks)
+    lay = B.cq_pack_info(300, 8192, 128, 4)
+    db, dq, ds = dev(blob), dev(q), dev(s)
+    runs = [host(B.cq_gemv(db, lay, codebooks[4], dq, ds)) for _ in range(3)]
+    assert all(np.array_equal(r.view(np.uint32), runs[0].view(np.uint32)) for r in runs[1:])
 
 
 # ------------------------------------------------ full sizes, sampled outputs
