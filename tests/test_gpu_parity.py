@@ -344,6 +344,10 @@ def test_graph_replays_match_eager(codebooks):
     blob3 = B.cq_pack(w3, lay3, codebooks[3])
     layt = B.cq_pack_info(200, 1024, 128, ocq.TERNARY_B3)
     blobt = B.cq_pack(w3, layt, None)
+    wk = torch.from_numpy(weights(rng, 100, 8192)).to(DEV)
+    layk = B.cq_pack_info(100, 8192, 128, 4)
+    blobk = B.cq_pack(wk, layk, cb)
+    qk, sk = B.act_fwht_quant_a8(dev(inputs.activations(rng, 12, 8192)))
     wq = torch.from_numpy(inputs.weight_matrix(rng, 312, 1092)).to(DEV)
     blk = B.q4_0_pack(wq)
     x1, x4 = (dev(inputs.activations(rng, b, 4096)) for b in (1, 4))
@@ -351,10 +355,11 @@ def test_graph_replays_match_eager(codebooks):
     xq, xqm = (dev(inputs.activations(rng, b, 1092)) for b in (1, 37))
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=DEV)
     y1, y4, yp, yq, yqm, yt = f32(1, 300), f32(4, 300), f32(70, 200), f32(1, 312), f32(37, 312), f32(70, 200)
+    yk = f32(12, 100)
     qp = torch.empty((70, 1024), dtype=torch.int8, device=DEV)
     sp = f32(70)
     blob_out = torch.empty_like(blob)
-    outs = [y1, y4, qp, sp, yp, yq, yqm, blob_out, yt]
+    outs = [y1, y4, qp, sp, yp, yq, yqm, blob_out, yt, yk]
 
     def step():
         B.cq_gemv_f32(blob, lay, cb, x1, y=y1)                 # VALU GEMV, A8 fused
@@ -362,6 +367,7 @@ def test_graph_replays_match_eager(codebooks):
         B.act_fwht_quant_a8(xp, q=qp, scale=sp)
         B.cq_gemm(blob3, lay3, codebooks[3], qp, sp, y=yp)
         B.cq_gemm(blobt, layt, None, qp, sp, y=yt)             # base-3 ternary GEMM
+        B.cq_gemv(blobk, layk, cb, qk, sk, y=yk)               # K split: zero fill, atomic halves
         B.q4_0_gemv(blk, 312, 1092, xq, y=yq)
         B.q4_0_gemm(blk, 312, 1092, xqm, y=yqm)
         B.cq_pack(w, lay, cb, blob=blob_out)
