@@ -546,13 +546,32 @@ def bench_q4_0_prefill(B, torch, dev, steps, warmup, m=512):
         g.replay()
     ms = t.stop_ms() / steps
     tf = flops / ms / 1e9
+    # stacked: each layer's q, k, v as one [520, 312] matrix and gate, up as
+    # one [2184, 312] (the matrices that read the same activations), 41 launches
+    per = len(inputs.MINUEZA_LAYER_SHAPES)
+    stacked = []
+    for base in range(0, len(items) - 1, per):
+        for grp in ((0, 1, 2), (3,), (4, 5), (6,)):
+            its = [items[base + i] for i in grp]
+            rows_s = sum(it[1] for it in its)
+            stacked.append((rows_s, its[0][2], torch.cat([it[3] for it in its]), its[0][4],
+                            torch.empty((m, rows_s), dtype=torch.float32, device=dev)))
+    stacked.append(items[-1][1:])
+
+    def stacked_pass():
+        for rows, cols, blocks, x, y in stacked:
+            B.q4_0_gemm(blocks, rows, cols, x, y=y)
+
+    ms_st = graph_mean_ms(torch, [stacked_pass] * max(steps, 5))
     # the head alone (32002 x 312: the one launch large enough to fill the chip)
     _, rows, cols, blocks, x, y = items[-1]
     d = graph_mean_ms(torch, [(lambda: B.q4_0_gemm(blocks, rows, cols, x, y=y))] * 8)
     head_tf = 2 * m * rows * cols / d / 1e9
     return dict(tokens=m, launches=len(items), gflop=flops / 1e9, us_graph=ms * 1e3,
-                tflops=tf, frac=tf / FP32_MFMA_PEAK_TFLOPS, head_us=d * 1e3, head_tflops=head_tf,
-                head_frac=head_tf / FP32_MFMA_PEAK_TFLOPS)
+                tflops=tf, frac=tf / FP32_MFMA_PEAK_TFLOPS, stacked_launches=len(stacked),
+                stacked_us_graph=ms_st * 1e3, stacked_tflops=flops / ms_st / 1e9,
+                stacked_frac=flops / ms_st / 1e9 / FP32_MFMA_PEAK_TFLOPS, head_us=d * 1e3,
+                head_tflops=head_tf, head_frac=head_tf / FP32_MFMA_PEAK_TFLOPS)
 
 
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix, published
@@ -597,6 +616,27 @@ def bench_q4_0_a8(B, torch, dev, steps, warmup, m=512):
             B.q4_0_gemv_a8_f32(blocks, rows, cols, x, y=y)
 
     d_a8, d_prod, d_fused = t(one(dec, False, True)), t(one(dec, False, False)), t(fused)
+    # stacked as in the fp32 passes: q, k, v one matrix, gate, up one (41 launches a pass)
+    per = len(inputs.MINUEZA_LAYER_SHAPES)
+
+    def stack(items, nt):
+        out = []
+        for base in range(0, len(items) - 1, per):
+            for grp in ((0, 1, 2), (3,), (4, 5), (6,)):
+                its = [items[base + i] for i in grp]
+                rows_s = sum(it[0] for it in its)
+                out.append((rows_s, its[0][1], torch.cat([it[2] for it in its]), its[0][3], its[0][4], its[0][5],
+                            torch.empty((nt, rows_s), dtype=torch.float32, device=dev)))
+        out.append(items[-1])
+        return out
+
+    dec_st, pre_st = stack(dec, 1), stack(pre, m)
+
+    def fused_st():
+        for rows, cols, blocks, x, q, s, y in dec_st:
+            B.q4_0_gemv_a8_f32(blocks, rows, cols, x, y=y)
+
+    d_fused_st, p_prod_st = t(fused_st), t(one(pre_st, True, False))
     p_a8, p_prod = t(one(pre, True, True)), t(one(pre, True, False))
     rows, cols, blocks, x, q, s, y = pre[-1]
     head = sorted(graph_repeats_ms(torch, [lambda: B.q4_0_gemm_a8(blocks, rows, cols, q, s, y=y)] * 8))[2]
@@ -604,9 +644,11 @@ def bench_q4_0_a8(B, torch, dev, steps, warmup, m=512):
     return dict(
         decode=dict(launches=2 * len(dec), bytes=total, us_with_a8=d_a8 * 1e3, us_products_only=d_prod * 1e3,
                     gbps_products_only=total / d_prod / 1e6, us_fused=d_fused * 1e3, fused_launches=len(dec),
+                    us_fused_stacked=d_fused_st * 1e3, stacked_launches=len(dec_st),
                     note="weights warm in the Infinity Cache; us_fused: q4_0_gemv_a8_f32, the codes formed "
                          "in each product's launch"),
         prefill=dict(tokens=m, gop=flops / 1e9, us_with_a8=p_a8 * 1e3, us_products_only=p_prod * 1e3,
+                     us_products_only_stacked=p_prod_st * 1e3,
                      tops_products_only=flops / p_prod / 1e9,
                      frac_int8_peak=flops / p_prod / 1e9 / INT8_MFMA_PEAK_TOPS,
                      head_us=head * 1e3, head_tops=head_tops, head_frac_int8_peak=head_tops / INT8_MFMA_PEAK_TOPS))

@@ -281,7 +281,8 @@ def test_q4_0_gemv_parity(rows, cols, batch):
 def test_q4_0_stacked_rows_match_separate():
     """Matrices that read the same activations (a layer's q, k, v; gate and
     up), stacked row-wise into one launch, give every row bit for bit the
-    result of its own matrix's launch."""
+    result of its own matrix's GEMV launch, and its GEMM result to fp32
+    roundoff."""
     rng = np.random.default_rng(1300)
     for group in (((312, 312), (104, 312), (104, 312)), ((1092, 312), (1092, 312)), ((40, 1092), (300, 1092))):
         cols = group[0][1]
@@ -290,6 +291,14 @@ def test_q4_0_stacked_rows_match_separate():
         ys = np.concatenate([host(B.q4_0_gemv(b, r, cols, x)) for b, (r, _) in zip(blks, group)], axis=1)
         yst = host(B.q4_0_gemv(torch.cat(blks), sum(r for r, _ in group), cols, x))
         assert np.array_equal(ys.view(np.uint32), yst.view(np.uint32)), group
+        # prefill: the stacked GEMM may take another tile (another order of the
+        # fp32 sums), so rows agree to fp32 roundoff
+        xm = inputs.activations(rng, 64, cols)
+        ym = np.concatenate([host(B.q4_0_gemm(b, r, cols, dev(xm))) for b, (r, _) in zip(blks, group)], axis=1)
+        ymst = host(B.q4_0_gemm(torch.cat(blks), sum(r for r, _ in group), cols, dev(xm)))
+        mag = np.concatenate([omm.q4_0_magnitude(host(b).reshape(r, -1, 18), cols, xm) for b, (r, _) in zip(blks, group)],
+                             axis=1)
+        assert np.all(np.abs(ym - ymst) <= 2 * P.TOL_F32 * mag), group
 
 
 # tall matrices of 9..16 blocks a row take the persistent row-tile kernel
