@@ -270,6 +270,10 @@ __device__ __forceinline__ float oct_xor4(float v) {
   const int m = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true);
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));
 }
+// Lane i reads lane i^8 of its row of sixteen: the row rotated by 8.
+__device__ __forceinline__ float row_xor8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+}
 
 // Kernel shape: at most one workgroup per CU (more only for very tall
 // matrices), each finishing a contiguous run of rows.
@@ -294,12 +298,13 @@ __device__ __forceinline__ float oct_xor4(float v) {
 //     fixed order and writes y with coalesced stores.
 //
 // FUSED runs the A8 step on fp32 x with the same fp32 operations as
-// act_fwht_quant_a8: a thread holds one 16-element segment of a group in
-// registers, runs the four in-register butterfly stages, then the three
-// stages across the eight lanes of the group with DPP permutations (every
-// butterfly is the same a + b, a - b on the same operands, so the values
-// match the other kernel's bit for bit); block max, s = max / 127, and the
-// codes go straight from registers to LDS.
+// act_fwht_quant_a8: a thread holds KSEG-element segments of a group in
+// registers (16, or 8 for one token past 8192 columns), runs the in-register
+// butterfly stages (4, or 3), then the stages across the lanes of the group
+// (8 lanes: 3 stages, or 16 lanes: 4) with DPP permutations (every butterfly
+// is the same a + b, a - b on the same operands, so the values match the
+// other kernel's bit for bit); block max, s = max / 127, and the codes go
+// straight from registers to LDS.
 //
 // Work split: a row slot of P lanes (P = 64, or fewer for short rows) owns a
 // row; its 32-index chunks are dealt out as slot s -> chunk li + P * s.  A
@@ -309,15 +314,16 @@ __device__ __forceinline__ float oct_xor4(float v) {
 // IB: index bits (1..4).  BATCH: tokens per launch (1, 2, 4).  CPL: chunks a
 // lane handles per work item.  QREG: activations held in registers (NP == 1).
 // PD: work items in flight per wave.  FULL: P == 64 (the row sum reduces with
-// DPP).  FUSED: fp32 activations in, A8 done in the prologue.
-template <int IB, int BATCH, int CPL, bool QREG, int PD, bool FULL, bool FUSED>
+// DPP).  FUSED: fp32 activations in, A8 done in the prologue.  KSEG: the
+// fused prologue's segment length (16 or 8).
+template <int IB, int BATCH, int CPL, bool QREG, int PD, bool FULL, bool FUSED, int KSEG>
 __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs A, LevelTable T) {
   constexpr int TB = table_bytes<IB>();
   constexpr int kThreads = block_threads<CPL>();
   constexpr int kWaves = kThreads / kWave;
   constexpr int kCB = 4 * IB;                       // bytes of one chunk
   static_assert(FULL || CPL == 1, "short row slots take one chunk per item");
-  constexpr int kSeg = 16;                          // fused A8: elements a thread holds per segment
+  constexpr int kSeg = KSEG;                        // fused A8: elements a thread holds per segment
   constexpr int SEGS = FUSED ? (BATCH * kMaxFusedCols / kSeg + kThreads - 1) / kThreads : 1;
   constexpr int QV = FUSED ? 1 : (int)((kMaxActLds / 2 + 16 * kThreads - 1) / (16 * kThreads));
   __shared__ __align__(16) uint8_t tab[TB];
@@ -488,6 +494,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
     const float sg1 = (lane & 1) ? -1.0f : 1.0f;
     const float sg2 = (lane & 2) ? -1.0f : 1.0f;
     const float sg4 = (lane & 4) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
 #pragma unroll
     for (int j = 0; j < SEGS; ++j) {
       if (wave * kWave + j * kThreads >= nseg) continue;   // wave-uniform
@@ -503,14 +510,20 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
           }
         }
       }
-      // stages 16, 32 and 64: the partner element sits in lane ^ 1, ^ 2, ^ 4;
-      // the lower lane forms a + b, the upper one a - b (its own value is b)
+      // the stages across lanes (16, 32, 64, and 128 / 8 = 8 elements a
+      // thread: stage 8 also): the partner element sits in lane ^ 1, ^ 2, ^ 4
+      // (and ^ 8); the lower lane forms a + b, the upper one a - b (its own
+      // value is b)
 #pragma unroll
       for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg1, v[i], quad_xor1(v[i]));
 #pragma unroll
       for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg2, v[i], quad_xor2(v[i]));
 #pragma unroll
       for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg4, v[i], oct_xor4(v[i]));
+      if constexpr (kSeg == 8) {
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i) v[i] = fmaf(sg8, v[i], row_xor8(v[i]));
+      }
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < kSeg; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
       const int sg = t + j * kThreads;
       if (sg < nseg) {
         const int b = BATCH == 1 ? 0 : sg / spr, k0 = (sg - b * spr) * kSeg;
-        const int c = k0 >> 5, i0 = (k0 & 31) >> 3;     // chunk, and its first quarter (0 or 2)
+        const int c = k0 >> 5, i0 = (k0 & 31) >> 3;     // chunk, and its (first) quarter
         float sc = scs[0], inv = invs[0];
 #pragma unroll
         for (int bb = 1; bb < BATCH; ++bb)
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
         // codes in blocks of 8 (bounded register use), packed to fp16 pairs
         uint32_t pr[8];
 #pragma unroll
-        for (int k8 = 0; k8 < 2; ++k8) {
+        for (int k8 = 0; k8 < kSeg / 8; ++k8) {
           float ub[8], cb[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ub[i] = xv[j][8 * k8 + i];
@@ -558,7 +571,8 @@ __global__ __launch_bounds__(block_threads<CPL>()) void cq_gemv_kernel(GemvArgs 
             pr[4 * k8 + p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cb[2 * p], cb[2 * p + 1]));
         }
         *reinterpret_cast<uint4 *>(&qs[((b * 4 + i0) * C + c) * 4]) = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-        *reinterpret_cast<uint4 *>(&qs[((b * 4 + i0 + 1) * C + c) * 4]) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+        if constexpr (kSeg == 16)
+          *reinterpret_cast<uint4 *>(&qs[((b * 4 + i0 + 1) * C + c) * 4]) = make_uint4(pr[4], pr[5], pr[6], pr[7]);
       }
     }
   } else {
@@ -787,11 +801,20 @@ hipError_t launch_one(const uint8_t *blob, const bqm_cq_layout &L, const LevelTa
   if constexpr (CPL == 1) {
     // rows shorter than 64 chunks: several rows per wave (only ever one chunk per lane)
     if (cfg.plog2 < 6) {
-      cq_gemv_kernel<IB, BATCH, CPL, QREG, PD, false, FUSED><<<blocks, kThreads, qbytes, s>>>(A, T);
+      cq_gemv_kernel<IB, BATCH, CPL, QREG, PD, false, FUSED, 16><<<blocks, kThreads, qbytes, s>>>(A, T);
       return hipGetLastError();
     }
   }
-  cq_gemv_kernel<IB, BATCH, CPL, QREG, PD, true, FUSED><<<blocks, kThreads, qbytes, s>>>(A, T);
+  // fused A8 of one token with more than 8192 columns: 8-element segments, two
+  // a thread for most threads (measured faster there; slower at 4096 columns,
+  // where one 16-element segment a thread keeps a quarter of the threads busy)
+  if constexpr (FUSED && BATCH == 1 && CPL >= 2) {
+    if (L.cols > 8192) {
+      cq_gemv_kernel<IB, BATCH, CPL, QREG, PD, true, FUSED, 8><<<blocks, kThreads, qbytes, s>>>(A, T);
+      return hipGetLastError();
+    }
+  }
+  cq_gemv_kernel<IB, BATCH, CPL, QREG, PD, true, FUSED, 16><<<blocks, kThreads, qbytes, s>>>(A, T);
   return hipGetLastError();
 }
 
@@ -802,7 +825,7 @@ hipError_t launch_one(const uint8_t *blob, const bqm_cq_layout &L, const LevelTa
 template <int BATCH, int CPL, bool FUSED>
 constexpr int max_pd() {
   constexpr int kThreads = block_threads<CPL>();
-  constexpr int kSeg = 16;                          // as in the kernel
+  constexpr int kSeg = 16;                          // as in the kernel (KSEG 8: the same register count)
   constexpr int XREGS = FUSED ? (BATCH * kMaxFusedCols / kSeg + kThreads - 1) / kThreads * kSeg : 0;
   return (XREGS > 32 ? kRingChunks / 2 : kRingChunks) / CPL;
 }

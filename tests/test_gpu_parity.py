@@ -180,7 +180,10 @@ def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
 @pytest.mark.parametrize("rows,cols,batch", [(300, 512, 1), (130, 4096, 1), (67, 14336, 1),
                                              (1024, 4096, 1), (70, 4096, 4), (33, 1024, 16),
                                              (5, 128, 2), (1, 256, 1), (200, 4096, 3),
-                                             (129, 640, 16), (300, 4096, 7), (50, 5120, 3)])
+                                             (129, 640, 16), (300, 4096, 7), (50, 5120, 3),
+                                             # one token past 8192 columns: 8-element
+                                             # segments (8320: 1040 of them, 16384: two a thread)
+                                             (40, 8320, 1), (9, 16384, 1)])
 def test_cq_gemv_f32_fused_matches_two_step(code, rows, cols, batch, codebooks):
     """One-launch A8 + GEMV: the codes and scales equal the oracle's bit for bit and y
     equals the two-launch path (act_fwht_quant_a8, then cq_gemv) bit for bit."""
