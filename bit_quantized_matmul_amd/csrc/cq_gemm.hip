@@ -38,9 +38,10 @@
 //    WM x (4 / WM) grid of MB x NB MFMA tiles of 32 x 32 each.  A wave's LDS
 //    reads per step are MB A fragments and NB level lookups, and its VALU
 //    work (address perms, norm multiplies) scales with NB alone, so the
-//    tiles use tall waves: 128 x 64 each in the wide tile, 64 x 32 in the
-//    64 x 128 one (a 2 x 2 grid of 32 x 64 waves there spent ~11 VALU
-//    instructions per MFMA, against ~7 now).  The launch takes the largest
+//    tiles use tall waves side by side: 128 x 64 each in the wide tile,
+//    128 x 32 in the 128 x 128 one and 64 x 32 in the 64 x 128 one (2 x 2
+//    grids of 64 x 64 and 32 x 64 waves spent ~7 and ~11.5 VALU instructions
+//    per MFMA there, against ~5 and ~7).  The launch takes the largest
 //    workgroup tile that still gives every CU work (128 x 256 for wide
 //    matrices, 128 x 128, or 64 x 128).  Consecutive tiles (the m-tiles of one
 //    n-block, which share weights) are mapped to the same XCD: hardware deals
@@ -560,7 +561,7 @@ hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTab
   if (tiles(128, 256) >= (long)num_cus * 7 / 8)
     return launch_tiles<IB, 1, 4, 2>(blob, L, T, q, scale, m, y, s);
   if (tiles(128, 128) >= (long)num_cus * 7 / 8)
-    return launch_tiles<IB, 2, 2, 2>(blob, L, T, q, scale, m, y, s);
+    return launch_tiles<IB, 1, 4, 1>(blob, L, T, q, scale, m, y, s);
   if (tiles(64, 128) >= (long)num_cus * 7 / 8)
     return launch_tiles<IB, 1, 2, 1>(blob, L, T, q, scale, m, y, s);
   return launch_tiles<IB, 2, 1, 1>(blob, L, T, q, scale, m, y, s);

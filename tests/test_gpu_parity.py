@@ -269,6 +269,21 @@ def test_cq_gemm_parity(code, m, rows, cols, codebooks):
     P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_FOLD, f"cq_gemm code {code} m{m} {rows}x{cols}")
 
 
+# One shape per prefill tile, compared element by element.  The launch takes
+# the largest tile whose count reaches 7/8 of the CUs; on a 256-CU MI355X,
+# 500 tokens (ragged m-tiles) with 3600 rows take 64x128, with 7300 rows
+# 128x128, with 14100 rows 128x256 (every one with a ragged n-tile).  K of 8
+# groups loads the norms 8 to a load, K of 9 groups one by one.
+@pytest.mark.parametrize("rows", [3600, 7300, 14100])
+@pytest.mark.parametrize("cols", [1024, 1152])
+def test_cq_gemm_every_tile(rows, cols, codebooks):
+    rng = np.random.default_rng(1500 + rows + cols)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, 4, 500, codebooks)
+    lay = B.cq_pack_info(rows, cols, 128, 4)
+    y = host(B.cq_gemm(dev(blob), lay, host_codebook(4, codebooks), dev(q), dev(s)))
+    P.check_cq(y, idx, n16, 128, 4, lv, q, s, P.TOL_FOLD, f"cq_gemm tile case m500 {rows}x{cols}")
+
+
 @pytest.mark.parametrize("rows,cols,batch", [(312, 312, 1), (104, 312, 1), (1092, 312, 1),
                                              (312, 1092, 1), (300, 40, 3), (7, 1000, 16),
                                              (33, 33, 2)])
