@@ -628,9 +628,12 @@ hipError_t launch_cq_t3_gemm(const uint8_t *blob, const bqm_cq_layout &L, const 
   A.q_bytes = (uint32_t)((int64_t)m * L.cols);
   A.cfac = T.cscale / (float)kGroup;
   auto tiles = [&](int bm, int bn) { return (long)((m + bm - 1) / bm) * ((L.rows + bn - 1) / bn); };
+  // the largest tile that covers 7/8 of the CUs in one round; one round of
+  // larger tiles on at least half the CUs beats two rounds of smaller ones
   const long want = (long)num_cus * 7 / 8;
-  if (tiles(128, 256) >= want) return launch_t3_gemm_tiles<2, 1, 8>(A, s);
-  if (tiles(128, 128) >= want) return launch_t3_gemm_tiles<2, 1, 4>(A, s);
+  const long t256 = tiles(128, 256), t128 = tiles(128, 128), t64 = tiles(64, 128);
+  if (t256 >= want || (t128 > num_cus && 2 * t256 >= num_cus)) return launch_t3_gemm_tiles<2, 1, 8>(A, s);
+  if (t128 >= want || (t64 > num_cus && 2 * t128 >= num_cus)) return launch_t3_gemm_tiles<2, 1, 4>(A, s);
   return launch_t3_gemm_tiles<1, 1, 4>(A, s);
 }
 
