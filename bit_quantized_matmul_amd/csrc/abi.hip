@@ -274,17 +274,26 @@ int cq_gemv_f32(const void *blob, const bqm_cq_layout *layout, const float *code
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
   const bool base3 = layout->bits == BQM_CQ_TERNARY_B3;
-  // base-3: the A8 step goes to the caller's code buffers, then the product
+  // rows too wide for the fused launch: the A8 step into the caller's code
+  // buffers, then the cq_gemv product (as base-3 always does)
+  const bool two_step = !base3 && !cq_gemv_supported(*layout, true) && q_out && scale_out &&
+                        cq_gemv_supported(*layout, false);
   if (base3 ? (!cq_gemv_t3_supported(*layout, batch) || !q_out || !scale_out ||
                layout->cols > 65536)
-            : (batch > 16 || !cq_gemv_supported(*layout, true)))
+            : (batch > 16 || !(two_step || cq_gemv_supported(*layout, true))))
     return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(x) || ((uintptr_t)q_out & 3u) || ((uintptr_t)scale_out & 3u) ||
-      ((uintptr_t)y & 3u) || (base3 && !aligned16(q_out)))
+      ((uintptr_t)y & 3u) || ((base3 || two_step) && !aligned16(q_out)))
     return BQM_EALIGN;
   int cus;
   rc = current_device(&cus);
   if (rc) return rc;
+  if (two_step) {
+    const hipError_t e = launch_act_fwht_quant_a8(x, batch, layout->cols, q_out, scale_out, (hipStream_t)stream);
+    if (e != hipSuccess) return BQM_EDEVICE;
+    return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q_out, scale_out, batch, y, cus,
+                                    (hipStream_t)stream));
+  }
   if (base3) {
     const hipError_t e = launch_act_fwht_quant_a8(x, batch, layout->cols, q_out, scale_out, (hipStream_t)stream);
     if (e != hipSuccess) return BQM_EDEVICE;

@@ -112,7 +112,8 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * (each finite and bfloat16-representable, hence exact in fp16 too;
  * BQM_EINVAL otherwise), NULL for bits 1, 5 and 6; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
- * 1 <= batch <= 16 (BQM_ENOTSUP above).  group must be 128.  For batch >= 2
+ * 1 <= batch <= 16 and cols <= 36864 (one token's codes as fp16 fit in LDS
+ * beside the level table; BQM_ENOTSUP past either).  group must be 128.  For batch >= 2
  * (>= 3 when cols > 4096) and cols <= 16384 the product runs on the matrix
  * cores in one pass over the weights for all tokens: exact fp16 levels x
  * exact fp16 codes, fp32 accumulation per group, fp32 norm per group, the
@@ -141,12 +142,15 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
  * product.  x [device] fp32 [batch, cols], 16-byte aligned; y [device] fp32
  * [batch, rows]; q_out [device, may be NULL] int8 [batch, cols] and scale_out
  * [device, may be NULL] fp32 [batch] receive the int8 codes and scales.
- * Other arguments and limits as cq_gemv, and cols <= 16384.  Where cq_gemv
- * would leave the VALU GEMV (see there) and both q_out (16-byte aligned) and
- * scale_out are given, the call runs as act_fwht_quant_a8 into them followed
- * by cq_gemv.  Otherwise one fused launch per 4 tokens: every workgroup
- * quantizes the activations itself while its first weight loads are in
- * flight, with the VALU GEMV's arithmetic.  y equals act_fwht_quant_a8 then
+ * Other arguments and limits as cq_gemv.  Where cq_gemv would leave the VALU
+ * GEMV (see there), or the rows have more than 16384 columns, and both q_out
+ * (16-byte aligned) and scale_out are given, the call runs as
+ * act_fwht_quant_a8 into them followed by cq_gemv; rows of more than 16384
+ * columns without them are BQM_ENOTSUP.  Otherwise one fused launch per 4
+ * tokens: every workgroup quantizes the activations itself while its first
+ * weight loads are in flight, with the VALU GEMV's arithmetic (a thread holds
+ * its segments of the row in registers, hence the 16384-column bound).
+ * y equals act_fwht_quant_a8 then
  * cq_gemv bit for bit for batch 1, and whenever q_out and scale_out are
  * given.  The library allocates nothing.  Base-3 ternary (bits 6): the
  * cq_gemv limits, and q_out (16-byte aligned) and scale_out are required

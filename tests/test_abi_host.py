@@ -98,8 +98,12 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv_f32(p, ctypes.byref(big), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
     over = binding.cq_pack_info(8, 16512, 128, 4)                      # one group past the fused limit
     assert lib.cq_gemv_f32(p, ctypes.byref(over), cb, p, 1, p, None, None, None) == E.BQM_ENOTSUP
+    # ... which runs in two launches into code buffers, 16-byte aligned, up to cq_gemv's width
+    assert lib.cq_gemv_f32(p, ctypes.byref(over), cb, p, 1, p, ctypes.c_void_p(4100), p, None) == E.BQM_EALIGN
+    assert lib.cq_gemv_f32(p, ctypes.byref(over), cb, p, 17, p, p, p, None) == E.BQM_ENOTSUP
     wide = binding.cq_pack_info(8, 36992, 128, 4)                      # one group past the int8 limit
     assert lib.cq_gemv(p, ctypes.byref(wide), cb, p, p, 1, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv_f32(p, ctypes.byref(wide), cb, p, 1, p, p, p, None) == E.BQM_ENOTSUP
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, None, 1, p, None, None, None) == E.BQM_EINVAL
     assert lib.cq_gemv_f32(p, ctypes.byref(lay), cb, p, 1, p, ctypes.c_void_p(4098), None, None) == E.BQM_EALIGN
     # base-3 ternary: the GEMV up to 16 tokens and 128 groups a row (the GEMM

@@ -439,6 +439,28 @@ def test_maximum_sizes(code, entry, rows, cols, batch, codebooks):
     P.check_cq(y, idx, n16, 128, code, lv, q, s, tol, f"max size {entry} code {code} {rows}x{cols} b{batch}")
 
 
+# rows wider than the fused launch's 16384 columns: with code buffers,
+# cq_gemv_f32 runs the A8 step into them and then cq_gemv (one token and three
+# tokens on the VALU GEMV, six on the GEMM kernel)
+@pytest.mark.parametrize("rows,cols,batch", [(33, 28672, 1), (20, 36864, 3), (9, 20480, 6)])
+def test_cq_gemv_f32_wide_rows(rows, cols, batch, codebooks):
+    rng = np.random.default_rng(1700 + rows + batch)
+    lv, idx, n16, blob, _, _ = oracle_case(rng, rows, cols, 4, batch, codebooks)
+    x = inputs.activations(rng, batch, cols)
+    q_ref, s_ref = oa8.act_quant_a8(x, 128, "fp32")
+    lay = B.cq_pack_info(rows, cols, 128, 4)
+    db = dev(blob)
+    q_out = torch.empty((batch, cols), dtype=torch.int8, device=DEV)
+    s_out = torch.empty(batch, dtype=torch.float32, device=DEV)
+    y = host(B.cq_gemv_f32(db, lay, codebooks[4], dev(x), q_out=q_out, scale_out=s_out))
+    assert np.array_equal(host(q_out), q_ref)
+    assert np.array_equal(host(s_out).view(np.uint32), s_ref.view(np.uint32))
+    y2 = host(B.cq_gemv(db, lay, codebooks[4], q_out, s_out))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    tol = P.TOL_FOLD if batch > 4 else P.cq_gemv_tol(cols, batch)
+    P.check_cq(y, idx, n16, 128, 4, lv, q_ref, s_ref, tol, f"cq_gemv_f32 wide rows {rows}x{cols} b{batch}")
+
+
 def test_results_are_deterministic(codebooks):
     rng = np.random.default_rng(700)
     lv, idx, n16, blob, q, s = oracle_case(rng, 300, 1024, 4, 40, codebooks)
