@@ -37,7 +37,7 @@ constexpr int kA8Threads = 256;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16a __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x3a __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
 
 // codes 0..7 of a group (dwords d0 = q0..q3, d1 = q4..q7) -> (q0, q2, q4, q6)
 // and (q1, q3, q5, q7)
@@ -371,9 +371,9 @@ hipError_t gemv_fused_batch(const uint8_t *blocks, int rows, int cols, int nblk,
 constexpr int kA8TileM = 64, kA8TileN = 64;       // tokens x weight rows per workgroup (KSPLIT 1)
 
 struct A8BlockIn {
-  uint32_t a[5];     // 20 code bytes from the aligned address below the lane's 16
-  u32x3a nib;        // 12 bytes from the aligned address below the lane's 8 nibble bytes
-  uint32_t dw;       // the aligned word holding the fp16 scale
+  u32x4a a;          // 16 code bytes from the aligned address below the lane's 16,
+  uint32_t a4;       // and the next 4
+  u32x4a w;          // 16 block bytes from the aligned word below the block, + 8 h
 };
 
 // KSPLIT: 1 (2 x 2 wave tiles of 32 x 32) or 4 (one 32 x 32 tile, the blocks
@@ -395,14 +395,16 @@ __global__ __launch_bounds__(kA8Threads) void q4_0_gemm_a8_kernel(
   const uint32_t qrow = tok < m ? (uint32_t)tok * (uint32_t)cols : kQ4OOB;
   const uint32_t wrow = row < rows ? (uint32_t)row * (uint32_t)nblk * kQ4BlockBytes : kQ4OOB;
 
+  // three loads a block: 20 code bytes as 16 + 4, and 16 block bytes, so
+  // that the loads per MFMA stay few (each load instruction is an address
+  // unit pass for the whole wave)
   auto load = [&](A8BlockIn &in, int b) {
     const uint32_t qo = qrow + (uint32_t)(kQ4Block * b + 16 * h);
     const uint32_t qa = qo & ~3u;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) in.a[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, qa + 4u * i, 0, 0);
+    in.a = __builtin_bit_cast(u32x4a, __builtin_amdgcn_raw_buffer_load_b128(rq, qa, 0, 0));
+    in.a4 = __builtin_amdgcn_raw_buffer_load_b32(rq, qa + 16u, 0, 0);
     const uint32_t bo = wrow + (uint32_t)b * kQ4BlockBytes;
-    in.dw = __builtin_amdgcn_raw_buffer_load_b32(rw, bo & ~3u, 0, 0);
-    in.nib = __builtin_bit_cast(u32x3a, __builtin_amdgcn_raw_buffer_load_b96(rw, (bo + 2u + 8u * h) & ~3u, 0, 0));
+    in.w = __builtin_bit_cast(u32x4a, __builtin_amdgcn_raw_buffer_load_b128(rw, (bo & ~3u) + 8u * h, 0, 0));
   };
 
   f32x16a acc;
@@ -412,17 +414,23 @@ __global__ __launch_bounds__(kA8Threads) void q4_0_gemm_a8_kernel(
     // codes 16h .. 16h + 15 of the block, realigned, as evens / odds of each 8
     const uint32_t qo = qrow + (uint32_t)(kQ4Block * b + 16 * h);
     const uint32_t sq = qo & 3u;
+    const uint32_t aw[5] = {in.a.x, in.a.y, in.a.z, in.a.w, in.a4};
     uint32_t c[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_alignbyte(in.a[i + 1], in.a[i], sq);
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_alignbyte(aw[i + 1], aw[i], sq);
     const i32x4 A = {(int)evens(c[1], c[0]), (int)odds(c[1], c[0]), (int)evens(c[3], c[2]), (int)odds(c[3], c[2])};
-    // nibble bytes 8h .. 8h + 7 (elements 16h ..), realigned; low nibbles are
-    // the even elements, high nibbles the odd ones
+    // nibble bytes 8h .. 8h + 7 (elements 16h ..), at byte (bo & 3) + 2 of the
+    // lane's window (2 or 4: blocks are 2-byte aligned), realigned; low
+    // nibbles are the even elements, high nibbles the odd ones.  The scale
+    // sits in the first word of the lower half's window; lane l32 + 32 (the
+    // same weight row) takes it from lane l32.
     const uint32_t bo = wrow + (uint32_t)b * kQ4BlockBytes;
-    const float d = half_bits_to_float((uint16_t)(in.dw >> ((bo & 2u) * 8u)));
-    const uint32_t sh = (bo + 2u + 8u * h) & 3u;
-    const uint32_t n0 = __builtin_amdgcn_alignbyte(in.nib.y, in.nib.x, sh);
-    const uint32_t n1 = __builtin_amdgcn_alignbyte(in.nib.z, in.nib.y, sh);
+    const uint32_t dlo = (uint32_t)__shfl_xor((int)in.w.x, 32, 64);
+    const float d = half_bits_to_float((uint16_t)((h ? dlo : in.w.x) >> ((bo & 2u) * 8u)));
+    const bool at4 = (bo & 2u) != 0;                 // nibbles start at byte 4: word 1
+    const uint32_t w0 = at4 ? in.w.y : in.w.x, w1 = at4 ? in.w.z : in.w.y, w2 = at4 ? in.w.w : in.w.z;
+    const uint32_t n0 = __builtin_amdgcn_alignbyte(w1, w0, at4 ? 0u : 2u);
+    const uint32_t n1 = __builtin_amdgcn_alignbyte(w2, w1, at4 ? 0u : 2u);
     const i32x4 Bv = {(int)nib_minus8(n0 & 0x0F0F0F0Fu), (int)nib_minus8((n0 >> 4) & 0x0F0F0F0Fu),
                       (int)nib_minus8(n1 & 0x0F0F0F0Fu), (int)nib_minus8((n1 >> 4) & 0x0F0F0F0Fu)};
     i32x16 zero;
