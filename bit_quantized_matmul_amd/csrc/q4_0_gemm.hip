@@ -26,7 +26,8 @@
 //    takes one 32 x 32 tile instead and its four waves split the blocks
 //    (wave w: blocks w, w + 4, ...); their sums meet in LDS in a fixed order.
 //    An fp32 MFMA occupies a SIMD for 64 cycles, so the split is what shortens
-//    a small launch.
+//    a small launch.  Rows of at most 16 blocks take 16 x 16 tiles on
+//    v_mfma_f32_16x16x4_f32 instead (q4_0_gemm16_kernel), split the same way.
 //  * Blocks sit at 2-byte-aligned offsets: the nibble bytes come as the 12
 //    bytes from the 4-byte-aligned address below them, realigned with
 //    v_alignbyte; the scale as the aligned word holding it.
@@ -173,6 +174,112 @@ __global__ __launch_bounds__(kGemmThreads) void q4_0_gemm_kernel(
   }
 }
 
+// The small layer matrices: 16-token x 16-row tiles on v_mfma_f32_16x16x4_f32
+// (A = 16 tokens x 4 k, B = 4 k x 16 rows), four waves splitting the blocks
+// as above.  A 32 x 32 tile leaves most CUs idle on these shapes and makes
+// one wave run a chain of 16 fp32 MFMAs of 64 cycles per block; a 16 x 16 tile
+// needs 8 of 32 cycles, and four times as many workgroups share the CUs.
+// Within a block, lane quarter kq (= lane / 16) supplies elements 8 kq .. 8 kq
+// + 7 over the block's 8 steps (step s: element 8 kq + s), i.e. 32 contiguous
+// activation bytes and nibble bytes 4 kq .. 4 kq + 3, in the same order for A
+// and B.
+template <bool VEC>
+__global__ __launch_bounds__(kGemmThreads) void q4_0_gemm16_kernel(
+    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t block_bytes,
+    const float *__restrict__ x, uint32_t x_bytes, int m, float *__restrict__ y) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  constexpr int S = 4;                                             // waves splitting the blocks
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tok = blockIdx.y * 16 + r16;                           // A row of this lane
+  const int row = blockIdx.x * 16 + r16;                           // B column of this lane
+  const __amdgpu_buffer_rsrc_t rx = rsrc_q(x, x_bytes);
+  const __amdgpu_buffer_rsrc_t rw = rsrc_q(blocks, block_bytes);
+  const uint32_t xrow = tok < m ? (uint32_t)tok * (uint32_t)cols * 4u : kOOBq;
+  const uint32_t wrow = row < rows ? (uint32_t)row * (uint32_t)nblk * kQBlockBytes : kOOBq;
+
+  struct In {
+    float a[8];
+    uint32_t nib[2];   // 8 bytes from the aligned address below the lane's 4 nibble bytes
+    uint32_t dw;       // the aligned word holding the fp16 scale
+  };
+  auto load = [&](In &in, int b) {
+    const uint32_t xo = xrow + (uint32_t)(kQBlock * b + 8 * kq) * 4u;
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const f32x4q v = __builtin_bit_cast(f32x4q, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16u * i, 0, 0));
+        in.a[4 * i + 0] = v.x;
+        in.a[4 * i + 1] = v.y;
+        in.a[4 * i + 2] = v.z;
+        in.a[4 * i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        in.a[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, xo + 4u * i, 0, 0));
+    }
+    const uint32_t bo = wrow + (uint32_t)b * kQBlockBytes;
+    in.dw = __builtin_amdgcn_raw_buffer_load_b32(rw, bo & ~3u, 0, 0);
+    // two single-word loads: each is range-checked on its own, so a word past
+    // the end of the blocks reads 0 (and is then not among the bytes used)
+    const uint32_t no = (bo + 2u + 4u * kq) & ~3u;
+    in.nib[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, no, 0, 0);
+    in.nib[1] = __builtin_amdgcn_raw_buffer_load_b32(rw, no + 4u, 0, 0);
+  };
+  f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto multiply = [&](In &in, int b) {
+    if (b == nblk - 1 && (cols & (kQBlock - 1))) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (kQBlock * b + 8 * kq + s >= cols) in.a[s] = 0.0f;
+    }
+    const uint32_t bo = wrow + (uint32_t)b * kQBlockBytes;
+    const float d = half_bits_to_float((uint16_t)(in.dw >> ((bo & 2u) * 8u)));
+    const uint32_t q = __builtin_amdgcn_alignbyte(in.nib[1], in.nib[0], (bo + 2u + 4u * kq) & 3u) ^ 0x88888888u;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int v = __builtin_amdgcn_sbfe((int)q, 4 * s, 4);         // nibble - 8
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(in.a[s], (float)v * d, acc, 0, 0, 0);
+    }
+  };
+  const int last = nblk - 1, kw = wave;
+  In in0, in1;
+  load(in0, kw < nblk ? kw : last);
+  for (int b = kw; b < nblk; b += 2 * S) {
+    load(in1, b + S < nblk ? b + S : last);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(in0, b);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + S < nblk) {                          // uniform
+      load(in0, b + 2 * S < nblk ? b + 2 * S : last);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(in1, b + S);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // waves 1..3 hand their sums to wave 0, which adds them in wave order
+  __shared__ float part[S - 1][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < S - 1; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += part[w][r][lane];
+  // lane (r16, kq) holds weight row r16 of the tile for tokens 4 kq + r
+  if (row < rows) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = blockIdx.y * 16 + 4 * kq + r;
+      if (t < m) y[(size_t)t * rows + row] = acc[r];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_q4_0_gemm(const uint8_t *blocks, int rows, int cols, const float *x, int m,
@@ -186,6 +293,13 @@ hipError_t launch_q4_0_gemm(const uint8_t *blocks, int rows, int cols, const flo
   // blocks split over the four waves
   const long big = (long)((rows + kTileN - 1) / kTileN) * ((m + kTileM - 1) / kTileM);
   const bool split = big < num_cus && nblk > 1;
+  // 16 x 16 tiles for short rows (at most 16 blocks) while they stay within
+  // five workgroups a CU; past that, or for longer rows, the 32 x 32 tiles'
+  // fewer activation re-reads win (measured at 512 tokens: 104 x 312 3.4
+  // against 5.4 us, 312 x 312 4.9 against 5.5, 520 x 312 6.9 against 7.6;
+  // but 1092 x 312 10.9 against 9.4 and 312 x 1092 11.1 against 10.1)
+  const long t16n = (long)((rows + 15) / 16) * ((m + 15) / 16);
+  const bool t16 = split && nblk <= 16 && t16n <= 5L * num_cus;
   const int tm = split ? 32 : kTileM, tn = split ? 32 : kTileN;
   const dim3 grid((rows + tn - 1) / tn, (m + tm - 1) / tm);
   if (grid.y > 65535) return hipErrorInvalidValue;
@@ -197,6 +311,15 @@ hipError_t launch_q4_0_gemm(const uint8_t *blocks, int rows, int cols, const flo
   auto go = [&](auto kern) {
     kern<<<grid, kGemmThreads, 0, s>>>(blocks, rows, cols, nblk, range, x, (uint32_t)x_bytes, m, y);
   };
+  if (t16) {
+    const dim3 g16((rows + 15) / 16, (m + 15) / 16);
+    if (g16.y > 65535) return hipErrorInvalidValue;
+    if ((cols & 3) == 0)
+      q4_0_gemm16_kernel<true><<<g16, kGemmThreads, 0, s>>>(blocks, rows, cols, nblk, range, x, (uint32_t)x_bytes, m, y);
+    else
+      q4_0_gemm16_kernel<false><<<g16, kGemmThreads, 0, s>>>(blocks, rows, cols, nblk, range, x, (uint32_t)x_bytes, m, y);
+    return hipGetLastError();
+  }
   if ((cols & 3) == 0) {
     if (split) go(q4_0_gemm_kernel<true, 4>);
     else go(q4_0_gemm_kernel<true, 1>);
