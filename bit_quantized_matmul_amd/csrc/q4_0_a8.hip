@@ -26,7 +26,8 @@
 // weights as the low then the high nibbles of each nibble word, each turned
 // into the signed byte nibble - 8.  The int32 result of a block is scaled by
 // the lane's row scale d and added in fp32; tiles and the split of the
-// blocks over waves follow the fp32 Q4_0 GEMM.
+// blocks over waves follow the fp32 Q4_0 GEMM, with 16 x 16 tiles on
+// v_mfma_i32_16x16x32_i8 for the short rows of the small layer matrices.
 #include "bqm_common.h"
 #include "q4_0_block.h"
 
@@ -487,6 +488,94 @@ __global__ __launch_bounds__(kA8Threads) void q4_0_gemm_a8_kernel(
   }
 }
 
+// The small layer matrices: 16-token x 16-row tiles on v_mfma_i32_16x16x32_i8,
+// one block per instruction, the blocks split over the four waves as above.
+// Lane quarter kq (= lane / 16) supplies elements 8 kq .. 8 kq + 7 of a block
+// to both operands in the same order: the 8 codes as evens then odds, the 4
+// nibble bytes 4 kq .. 4 kq + 3 as their low then their high nibbles, each
+// turned into nibble - 8.  The int32 result of a block is scaled by the row's d
+// and added in fp32, as in the 32 x 32 kernel.  ALIGNED: cols % 4 == 0.
+template <bool ALIGNED>
+__global__ __launch_bounds__(kA8Threads) void q4_0_gemm_a8_16_kernel(
+    const uint8_t *__restrict__ blocks, int rows, int cols, int nblk, uint32_t block_bytes,
+    const int8_t *__restrict__ q, uint32_t q_bytes, const float *__restrict__ scale, int m,
+    float *__restrict__ y) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  constexpr int S = 4;                                             // waves splitting the blocks
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tok = blockIdx.y * 16 + r16;                           // A row of this lane
+  const int row = blockIdx.x * 16 + r16;                           // B column of this lane
+  const __amdgpu_buffer_rsrc_t rq = q4_rsrc(q, q_bytes);
+  const __amdgpu_buffer_rsrc_t rw = q4_rsrc(blocks, block_bytes);
+  const uint32_t qrow = tok < m ? (uint32_t)tok * (uint32_t)cols : kQ4OOB;
+  const uint32_t wrow = row < rows ? (uint32_t)row * (uint32_t)nblk * kQ4BlockBytes : kQ4OOB;
+
+  struct In {
+    uint32_t c0, c1;   // codes 8 kq .. 8 kq + 7 of the block
+    uint32_t n0, n1;   // the two words from the aligned address below the lane's nibble bytes
+    uint32_t dw;       // the aligned word holding the fp16 scale
+  };
+  auto load = [&](In &in, int b) {
+    load8<ALIGNED>(rq, qrow + (uint32_t)(kQ4Block * b + 8 * kq), in.c0, in.c1);
+    const uint32_t bo = wrow + (uint32_t)b * kQ4BlockBytes;
+    in.dw = __builtin_amdgcn_raw_buffer_load_b32(rw, bo & ~3u, 0, 0);
+    // single-word loads: a word past the end of the blocks reads 0 on its own
+    // (and is then not among the bytes used)
+    const uint32_t no = (bo + 2u + 4u * kq) & ~3u;
+    in.n0 = __builtin_amdgcn_raw_buffer_load_b32(rw, no, 0, 0);
+    in.n1 = __builtin_amdgcn_raw_buffer_load_b32(rw, no + 4u, 0, 0);
+  };
+  f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto multiply = [&](const In &in, int b) {
+    const uint32_t bo = wrow + (uint32_t)b * kQ4BlockBytes;
+    const float d = half_bits_to_float((uint16_t)(in.dw >> ((bo & 2u) * 8u)));
+    const uint32_t n = __builtin_amdgcn_alignbyte(in.n1, in.n0, (bo + 2u + 4u * kq) & 3u);
+    const uint64_t a = (uint64_t)evens(in.c1, in.c0) | ((uint64_t)odds(in.c1, in.c0) << 32);
+    const uint64_t w = (uint64_t)nib_minus8(n & 0x0F0F0F0Fu) | ((uint64_t)nib_minus8((n >> 4) & 0x0F0F0F0Fu) << 32);
+    const i32x4 zero = {0, 0, 0, 0};
+    const i32x4 isum = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)w, zero, 0, 0, 0);
+    // lane (r16, kq) holds column r16 (its own weight row, scale d)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(d, (float)isum[r], acc[r]);
+  };
+  const int last = nblk - 1, kw = wave;
+  In in0, in1;
+  load(in0, kw < nblk ? kw : last);
+  for (int b = kw; b < nblk; b += 2 * S) {
+    load(in1, b + S < nblk ? b + S : last);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(in0, b);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + S < nblk) {                          // uniform
+      load(in0, b + 2 * S < nblk ? b + 2 * S : last);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(in1, b + S);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // waves 1..3 hand their sums to wave 0, which adds them in wave order
+  __shared__ float part[S - 1][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < S - 1; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += part[w][r][lane];
+  // lane (r16, kq) holds weight row r16 of the tile for tokens 4 kq + r
+  if (row < rows) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = blockIdx.y * 16 + 4 * kq + r;
+      if (t < m) y[(size_t)t * rows + row] = acc[r] * scale[t];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_q4_0_gemv_a8(const uint8_t *blocks, int rows, int cols, const int8_t *q,
@@ -562,6 +651,22 @@ hipError_t launch_q4_0_gemm_a8(const uint8_t *blocks, int rows, int cols, const 
   const bool split = big < num_cus && nblk > 1;
   const int tm = split ? 32 : kA8TileM, tn = split ? 32 : kA8TileN;
   const dim3 grid((rows + tn - 1) / tn, (m + tm - 1) / tm);
+  // 16 x 16 tiles for short rows (at most 16 blocks) while they stay within
+  // five workgroups a CU, as in the fp32 Q4_0 GEMM (measured at 512 tokens:
+  // 104 x 312 3.3 against 5.1 us, 312 x 312 4.3 against 5.2; 1092 x 312 8.1
+  // against 6.5 and 312 x 1092 8.0 against 7.3 with them, so those keep 32 x 32)
+  const long t16n = (long)((rows + 15) / 16) * ((m + 15) / 16);
+  const bool t16 = split && nblk <= 16 && t16n <= 5L * num_cus;
+  if (t16) {
+    const dim3 g16((rows + 15) / 16, (m + 15) / 16);
+    if ((cols & 3) == 0)
+      q4_0_gemm_a8_16_kernel<true><<<g16, kA8Threads, 0, s>>>(blocks, rows, cols, nblk, (uint32_t)block_bytes, q,
+                                                               (uint32_t)q_bytes, scale, m, y);
+    else
+      q4_0_gemm_a8_16_kernel<false><<<g16, kA8Threads, 0, s>>>(blocks, rows, cols, nblk, (uint32_t)block_bytes, q,
+                                                                (uint32_t)q_bytes, scale, m, y);
+    return hipGetLastError();
+  }
   if (split)
     q4_0_gemm_a8_kernel<4><<<grid, kA8Threads, 0, s>>>(blocks, rows, cols, nblk, (uint32_t)block_bytes, q,
                                                        (uint32_t)q_bytes, scale, m, y);
