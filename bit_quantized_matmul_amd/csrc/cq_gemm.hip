@@ -93,8 +93,8 @@ __device__ __forceinline__ uint32_t perm_addr(uint32_t w, uint32_t laneoff) {
 
 // B operand for step s (0..3) of a lane's half group: the 8 levels of indices
 // 8s .. 8s+7 of its 32, whose codes sit in IB words (4*IB bytes).
-template <int IB>
-__device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[IB], int s,
+template <int IB, int NW>
+__device__ __forceinline__ f16x8 lookup_step(const uint32_t (&wd)[NW], int s,
                                              const uint8_t *tab, uint32_t laneoff) {
   uint32_t r[4];
   if constexpr (IB == 4) {           // one dword = 8 indices = 4 pair lookups
@@ -161,16 +161,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// The lane's 4*IB index bytes of one half group (32 indices): IB whole words.
-template <int IB>
-__device__ __forceinline__ void load_b_half(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[IB]) {
-  if constexpr (IB == 4) {
+// The lane's index bytes of one group for its steps (8 indices a step): NW
+// whole words (IB words for half a group's steps, IB / 2 for a quarter).
+template <int NW>
+__device__ __forceinline__ void load_b_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[NW]) {
+  if constexpr (NW == 4) {
     const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  } else if constexpr (IB == 3) {
+  } else if constexpr (NW == 3) {
     const u32x3 a = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
     w[0] = a.x; w[1] = a.y; w[2] = a.z;
-  } else if constexpr (IB == 2) {
+  } else if constexpr (NW == 2) {
     const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
     w[0] = a.x; w[1] = a.y;
   } else {
@@ -182,8 +183,10 @@ __device__ __forceinline__ void load_b_half(__amdgpu_buffer_rsrc_t r, uint32_t o
 // past M or N read zeros), all issued unconditionally so the compiler waits
 // for exactly one group's loads at a time; groups past K read zeros too, so
 // the loop runs a whole number of rounds with no branch.  N8: the group count
-// is a multiple of 8 and norms come 8 groups to a load.
-template <int IB, int WM, int MB, int NB, bool N8>
+// is a multiple of 8 and norms come 8 groups to a load.  KS: the split of
+// each group's 8 steps over the workgroup's waves (2: halves, four waves a
+// half; 4: quarters, two waves a quarter, for the narrow 64 x 32 tile).
+template <int IB, int WM, int MB, int NB, bool N8, int KS>
 __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     const uint8_t *__restrict__ idx, const uint16_t *__restrict__ norms,
     const int8_t *__restrict__ q, const float *__restrict__ scale, float *__restrict__ y,
@@ -192,8 +195,13 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   constexpr int TB = table_bytes<IB>();
   constexpr int kDepth = N8 ? 4 : 3;               // groups of A and B in flight per thread
   constexpr int kRound = N8 ? 8 : kDepth;          // groups per loop round (unrolled)
-  constexpr int WN = 4 / WM;
+  constexpr int kWPK = 8 / KS;                     // waves per k slice
+  constexpr int kSteps = 8 / KS;                   // 16-wide k steps of a wave per group
+  constexpr int kBW = kSteps * IB / 4;             // index words of a lane per group
+  constexpr int WN = kWPK / WM;
   constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * WN;
+  static_assert((KS == 2 || KS == 4) && kBW * 4 == kSteps * IB && WM * WN == kWPK,
+                "whole index words per lane and group; the waves of a slice tile it");
   constexpr int kAV = kBM / 64;                    // 16-byte A loads per thread per group
   constexpr int kYS = kBN + 8;                     // epilogue tile row stride (floats): rows 4 apart sit 32 banks apart
   constexpr int kLoopBytes = TB + 2 * kBM * kAStride * 2, kYBytes = kBM * kYS * 4;
@@ -207,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int kh = wave >> 2;                        // which half of each group's 8 steps
-  const int wm = (wave & 3) / WN, wn = (wave & 3) % WN;
+  const int kq = wave / kWPK;                      // which KS-th of each group's 8 steps
+  const int wm = (wave % kWPK) / WN, wn = (wave % kWPK) % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
   // XCD-aware tile order: tiles xcd*per .. xcd*per+per-1 run on one XCD
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   for (int nb = 0; nb < NB; ++nb) {
     ncol[nb] = n0 + 32 * NB * wn + 32 * nb + lr;
     const bool ok = ncol[nb] < N;
-    bbase[nb] = ok ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh + 4 * IB * kh) : kOOB;
+    bbase[nb] = ok ? (uint32_t)(ncol[nb] * row_bytes + 8 * IB * lh + kSteps * IB * kq) : kOOB;
     nbase[nb] = ok ? (uint32_t)(ncol[nb] * ng * 2) : kOOB;
   }
   // The row exponents: each lane needs e_n for its NB rows.  The two lanes of
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // load stays unconditional (no branch, no early vmcnt drain).
   auto kgroup = [&](int g) { const int x = g + rot; return g >= ng ? 0 : (x < ng ? x : x - ng); };
   u32x4 apre[kDepth][kAV];
-  uint32_t bpre[kDepth][NB][IB], npre[N8 ? 1 : kDepth][NB];
+  uint32_t bpre[kDepth][NB][kBW], npre[N8 ? 1 : kDepth][NB];
   u32x4 ncur[NB], nnext[NB];                       // N8: norms of this loop round's groups and the next one's
   auto issue_norms = [&](int g0, u32x4 (&dst)[NB]) {
     const int gg = kgroup(g0);
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
           ra, abase[i] + (uint32_t)(gg * kGroup), 0, 0));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      load_b_half<IB>(rb, bbase[nb] + (uint32_t)(gg * 16 * IB), bpre[slot][nb]);
+      load_b_words<kBW>(rb, bbase[nb] + (uint32_t)(gg * 16 * IB), bpre[slot][nb]);
       if constexpr (!N8)
         npre[slot][nb] = __builtin_amdgcn_raw_buffer_load_b32(rn, (nbase[nb] + 2u * gg) & ~3u, 0, 0);
     }
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   // changes); the workgroup barrier sits in the last chunk, where every wave
   // has written its part of the next group's A and read its last fragment of
   // this group's, followed by the next group's first A reads.
-  constexpr int kChunks = 4 * MB;
+  constexpr int kChunks = kSteps * MB;
   h2v nq[NB];
   f16x8 lvr[NB], bfr[2][NB], ar[3];
   auto scale_b = [&](const f16x8 &lv, h2v f) {
@@ -420,14 +428,14 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
       nq[nb] = h2v{h, h};
     }
   };
-  // lane's A fragment for chunk c: rows 32 (MB wm + mb) + lr, step 4 kh + s
-  const int afrag = (32 * MB * wm + lr) * kAStride + 64 * lh + 32 * kh;
+  // lane's A fragment for chunk c: rows 32 (MB wm + mb) + lr, step kSteps kq + s
+  const int afrag = (32 * MB * wm + lr) * kAStride + 64 * lh + 8 * kSteps * kq;
   auto read_a = [&](int buf, int c) {
     return *reinterpret_cast<const f16x8 *>(&As[buf][afrag + 32 * (c % MB) * kAStride + 8 * (c / MB)]);
   };
   take_group(0, 0, false);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[0][nb], 0, tab, laneoff);
+  for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB, kBW>(bpre[0][nb], 0, tab, laneoff);
   ar[0] = read_a(0, 0);
   if (kChunks > 1) ar[1] = read_a(0, 1);
 #pragma unroll
@@ -446,10 +454,12 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ar[c % 3], bfr[s & 1][nb], acc[mb][nb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (mb == 0) {
-          const int sl = s == 3 ? (d + 1) % kDepth : d;   // the last step looks up the next group
-          if (s == 3) take_group(g + 1, sl, d8 == kRound - 1);
+          const bool last = s == kSteps - 1;
+          const int sl = last ? (d + 1) % kDepth : d;   // the last step looks up the next group
+          if (last) take_group(g + 1, sl, d8 == kRound - 1);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) lvr[nb] = lookup_step<IB>(bpre[sl][nb], (s + 1) & 3, tab, laneoff);
+          for (int nb = 0; nb < NB; ++nb)
+            lvr[nb] = lookup_step<IB, kBW>(bpre[sl][nb], last ? 0 : s + 1, tab, laneoff);
         }
         if (c + 2 < kChunks) ar[(c + 2) % 3] = read_a(g & 1, c + 2);
         if (c >= 1 && c <= kAV) store_a_part((d + 1) % kDepth, (g + 1) & 1, c - 1);   // A of group g + 1
@@ -473,38 +483,34 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
     }
   }
 
-  // Epilogue through LDS (free now).  The two k-halves meet there: waves 4-7
-  // park their accumulators as an fp32 tile, waves 0-3 add theirs in place,
-  // then each row leaves as whole 16-byte chunks, so one store instruction
-  // writes a run of contiguous bytes.  MFMA D layout: register r of a lane
-  // holds row 8 (r / 4) + 4 lh + r % 4, column lr of its 32 x 32 tile.
+  // Epilogue through LDS (free now).  The KS k-slices meet there in a fixed
+  // order: the waves of the last slice park their accumulators as an fp32
+  // tile, those of each earlier slice in turn add theirs in place; then each
+  // row leaves as whole 16-byte chunks, so one store instruction writes a run
+  // of contiguous bytes.  MFMA D layout: register r of a lane holds row
+  // 8 (r / 4) + 4 lh + r % 4, column lr of its 32 x 32 tile.
   float *const ys = reinterpret_cast<float *>(smem);
   auto ypos = [&](int mb, int nb, int r) {
     return (32 * MB * wm + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3)) * kYS + 32 * NB * wn + 32 * nb + lr;
   };
   __syncthreads();                                 // every wave is done with the table and A buffers
   // (column lr of tile nb is weight row ncol[nb]: its 2^-e_n is exact)
-  if (kh == 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int j = KS - 1; j >= 0; --j) {
+    if (kq == j) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ys[ypos(mb, nb, r)] = acc[mb][nb][r] * rinv[nb];
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int p = ypos(mb, nb, r);
+            const float v = acc[mb][nb][r] * rinv[nb];
+            ys[p] = j == KS - 1 ? v : v + ys[p];
+          }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = ypos(mb, nb, r);
-          ys[p] = acc[mb][nb][r] * rinv[nb] + ys[p];
-        }
-  }
-  __syncthreads();
   const float cfac = T.cscale * (1.0f / kGroup);
   constexpr int kLPR = kBN / 4;                    // threads per tile row, 4 columns each
   constexpr int kRPP = kThreads / kLPR;            // rows per pass
@@ -529,10 +535,10 @@ __global__ __launch_bounds__(kThreads) void cq_gemm_kernel(
   }
 }
 
-template <int IB, int WM, int MB, int NB>
+template <int IB, int WM, int MB, int NB, int KS = 2>
 hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                         const int8_t *q, const float *scale, int m, float *y, hipStream_t s) {
-  constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * (4 / WM);
+  constexpr int kBM = 32 * MB * WM, kBN = 32 * NB * (8 / KS / WM);
   const int tiles_m = (m + kBM - 1) / kBM;
   const int tiles_n = (L.rows + kBN - 1) / kBN;
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
@@ -540,17 +546,18 @@ hipError_t launch_tiles(const uint8_t *blob, const bqm_cq_layout &L, const Level
   const uint32_t ib = (uint32_t)L.idx_bytes;
   const uint32_t nbytes = (uint32_t)((L.norms_count * 2 + 3) & ~(int64_t)3);   // whole words (blob pads to 64)
   if ((L.cols / kGroup) % 8 == 0)
-    cq_gemm_kernel<IB, WM, MB, NB, true><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+    cq_gemm_kernel<IB, WM, MB, NB, true, KS><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
                                                                    tiles_m, tiles_n, ib, nbytes, T);
   else
-    cq_gemm_kernel<IB, WM, MB, NB, false><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
+    cq_gemm_kernel<IB, WM, MB, NB, false, KS><<<grid, kThreads, 0, s>>>(blob, norms, q, scale, y, m, L.rows, L.cols,
                                                                     tiles_m, tiles_n, ib, nbytes, T);
   return hipGetLastError();
 }
 
 // Tile shape: the largest of 128x256, 128x128, 64x128 (m x n) whose tile count
-// still covers the CUs in one round, else 64x64 (few tokens: the launch is a
-// weight stream and wants every CU on it).  One round of larger tiles on at
+// still covers the CUs in one round, else 64x64, or 64x32 where even 64x64
+// leaves CUs idle (few tokens or rows: the launch is a weight stream and wants
+// every CU on it).  One round of larger tiles on at
 // least half the CUs beats two rounds of smaller ones (512 x 11008 x 4096:
 // 71 us in 172 tiles of 128 x 256 against 87 us in 344 of 128 x 128).
 template <int IB>
@@ -568,6 +575,12 @@ hipError_t launch_ib(const uint8_t *blob, const bqm_cq_layout &L, const LevelTab
     return launch_tiles<IB, 1, 4, 1>(blob, L, T, q, scale, m, y, s);
   if (t64 >= full)
     return launch_tiles<IB, 1, 2, 1>(blob, L, T, q, scale, m, y, s);
+  // fewer than 7/8 of the CUs with 64 x 64 tiles: 64 x 32 tiles (each group's
+  // steps in quarters, two 32 x 32 waves a quarter), twice the workgroups
+  // (measured: 512 x 1024 x 4096 20.5 against 22.7-23.8 us, 64 x 4096 x 4096
+  // 19.4 against 21.9, 32 x 4096 x 14336 53.5 against 64.7)
+  if constexpr (IB == 2 || IB == 4)
+    if (tiles(64, 64) < full) return launch_tiles<IB, 2, 1, 1, 4>(blob, L, T, q, scale, m, y, s);
   return launch_tiles<IB, 2, 1, 1>(blob, L, T, q, scale, m, y, s);
 }
 

@@ -284,6 +284,30 @@ def test_cq_gemm_every_tile(rows, cols, codebooks):
     P.check_cq(y, idx, n16, 128, 4, lv, q, s, P.TOL_FOLD, f"cq_gemm tile case m500 {rows}x{cols}")
 
 
+# Up to 32 tokens cq_gemm runs the decode kernels in launches of up to 16
+# tokens (exact fp16 products): those results meet the GEMV bar, which the
+# GEMM's one fp16 rounding a weight would not, and equal cq_gemv on each
+# 16-token slice bit for bit (17 tokens: a last launch of one token, the VALU
+# GEMV; 32: two matrix-core launches).  33 tokens take the GEMM (64 x 32
+# tiles for the 2- and 4-bit fields here: each group's steps in quarters).
+@pytest.mark.parametrize("code", [1, 2, 4, 5])
+@pytest.mark.parametrize("m", [17, 32, 33])
+def test_cq_gemm_few_tokens(code, m, codebooks):
+    rng = np.random.default_rng(1700 + code + m)
+    rows, cols = 300, 1024
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, code, m, codebooks)
+    lay = B.cq_pack_info(rows, cols, 128, code)
+    cb = host_codebook(code, codebooks)
+    y = host(B.cq_gemm(dev(blob), lay, cb, dev(q), dev(s)))
+    if m > 32:
+        P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_FOLD, f"cq_gemm code {code} m{m} 300x1024 (GEMM)")
+        return
+    P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"cq_gemm code {code} m{m} 300x1024 (decode kernels)")
+    for b0 in range(0, m, 16):
+        yb = host(B.cq_gemv(dev(blob), lay, cb, dev(q[b0:b0 + 16]), dev(s[b0:b0 + 16])))
+        assert np.array_equal(y[b0:b0 + 16], yb), f"tokens {b0}.."
+
+
 @pytest.mark.parametrize("rows,cols,batch", [(312, 312, 1), (104, 312, 1), (1092, 312, 1),
                                              (312, 1092, 1), (300, 40, 3), (7, 1000, 16),
                                              (33, 33, 2)])
