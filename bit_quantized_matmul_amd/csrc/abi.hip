@@ -158,7 +158,7 @@ int check_layout(const bqm_cq_layout *L) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? BQM_OK : BQM_EDEVICE; }
 
-constexpr int kGemvTokensForGemm = 32;   // cq_gemm: up to this many tokens run the GEMV kernels
+constexpr int kGemvTokensForGemm = 32;   // cq_gemm: up to this many tokens run the batched GEMV kernel
 
 // Scratch of cq_gemv_f32_noalloc: the int8 codes [batch, cols] and fp32
 // scales [batch] that cq_gemv_f32 stages in q_out / scale_out, for up to
@@ -370,19 +370,13 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
   if (base3)
     return status_of(launch_cq_t3_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
                                        (hipStream_t)stream));
-  // up to 32 tokens: the decode kernels in launches of up to 16 tokens read
-  // the weights once or twice and beat the GEMM's few tiles (measured at 32
-  // tokens: 4096x4096 11.6 against 19.0 us, 4096x14336 32.3 against 54.1;
-  // at 48 tokens the GEMM wins on 14336x4096, at 64 on every shape)
-  if (m <= kGemvTokensForGemm && cq_gemv_mma_supported(*layout, 16)) {
-    for (int b0 = 0; b0 < m; b0 += 16) {
-      const int nb = m - b0 < 16 ? m - b0 : 16;
-      const hipError_t e = launch_cq_gemv((const uint8_t *)blob, *layout, T, q + (size_t)b0 * layout->cols,
-                                          scale + b0, nb, y + (size_t)b0 * layout->rows, cus, (hipStream_t)stream);
-      if (e != hipSuccess) return BQM_EDEVICE;
-    }
-    return BQM_OK;
-  }
+  // up to 32 tokens: the batched decode kernel reads the weights once for all
+  // of them and beats the GEMM's few tiles (measured at 32 tokens: 4096x4096
+  // 10.8 against 19.0 us, 14336x4096 15.9 against 24.1, 4096x14336 21.0
+  // against 54.8; at 64 tokens, in two launches, the GEMM wins on three of
+  // the four shapes)
+  if (m <= kGemvTokensForGemm && cq_gemv_mma_supported(*layout, 16))
+    return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, m, y, cus, (hipStream_t)stream));
   return status_of(launch_cq_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
                                   (hipStream_t)stream));
 }

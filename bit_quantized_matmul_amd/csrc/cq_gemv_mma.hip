@@ -1,4 +1,4 @@
-// Batched decode GEMV (5..16 tokens) on packed CQ weights, on the matrix cores.
+// Batched decode GEMV (2..32 tokens) on packed CQ weights, on the matrix cores.
 //
 // "14MB holds 45M parameters: dissecting Needle's .cact file and W4A8
 // quantization", section 3: decode streams the pre-transposed [out, in] rows
@@ -25,6 +25,10 @@
 //    register rings, the next block's loads going out as a block is used
 //    (more in flight only delays the first block behind the queued loads).
 //  * The eighths of a row block meet once, through LDS, at the end.
+//  * 17..32 tokens (cq_gemm's few-token calls): two 16-token halves, each
+//    looked-up B fragment feeding one MFMA per half; the K chunk and the row
+//    blocks a workgroup takes are halved to make room for the second half's
+//    A fragments and partial sums.
 #include "bqm_common.h"
 
 namespace bqm {
@@ -33,13 +37,20 @@ namespace {
 constexpr int kThreadsV = 512;
 constexpr int kWaves = kThreadsV / 64;  // one per eighth of K
 constexpr int kTok = 16;                // token columns of the MFMA tile
+constexpr int kMaxTok = 2 * kTok;       // tokens a launch takes (two 16-token halves)
 constexpr int kRBMax = 8;               // row blocks a workgroup finishes
 constexpr int kChunkGroups = 32;        // K chunk: the groups whose codes the waves hold at once
+// With two token halves (TH = 2) a wave holds twice the A fragments and
+// partial sums: the K chunk and the row blocks a workgroup takes are halved.
+template <int TH> constexpr int chunk_groups() { return kChunkGroups / TH; }
+template <int TH> constexpr int rb_max() { return kRBMax / TH; }
 constexpr int kMaxCols = 16384;         // as the fused GEMV's limit
 constexpr int kMaxRings = 2;            // row blocks whose weights are in flight at once
 constexpr int kTabBytes = 65536;        // level table: 256-byte rows
-constexpr int kRedBytes = kWaves * kRBMax * 4 * 64 * 4;   // partial sums [wave][block][r][lane]
-static_assert(kTabBytes + kRedBytes <= 163840, "LDS of one CU");
+// partial sums [wave][block][half][r][lane]
+template <int NRB, int TH> constexpr int red_bytes() { return kWaves * NRB * TH * 4 * 64 * 4; }
+static_assert(kTabBytes + red_bytes<kRBMax, 1>() <= 163840 && kTabBytes + red_bytes<rb_max<2>(), 2>() <= 163840,
+              "LDS of one CU");
 constexpr uint32_t kOOBv = 0x80000000u;
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -200,11 +211,13 @@ struct MmaArgs {
 // row blocks' partial sums gather in LDS.  KS = 2: workgroups 2 j and 2 j + 1
 // take the two halves of K of the same row blocks, each reading only its
 // half's codes, and add their results into y, which the caller has zeroed:
-// two addends onto zero give the same sum in either order.
-template <int IB, int PD, int NRB, bool CHUNKED, int KS>
+// two addends onto zero give the same sum in either order.  TH: token halves
+// (1: up to 16 tokens; 2: up to 32, each B fragment feeding one MFMA per half).
+template <int IB, int PD, int NRB, bool CHUNKED, int KS, int TH>
 __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, LevelTable T) {
+  constexpr int kCG = chunk_groups<TH>();
   // one array, the table at its start: table addresses need no base added
-  __shared__ __align__(16) uint8_t lds[kTabBytes + kRedBytes];
+  __shared__ __align__(16) uint8_t lds[kTabBytes + red_bytes<NRB, TH>()];
   uint8_t *const tab = lds;
   float *const red = reinterpret_cast<float *>(lds + kTabBytes);
   const int t = threadIdx.x, lane = t & 63;
@@ -213,7 +226,7 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
   const int kh = KS == 1 ? 0 : (int)blockIdx.x % KS;           // this workgroup's part of K
   const int rg = KS == 1 ? (int)blockIdx.x : (int)blockIdx.x / KS;
   const int gb = kh * ng / KS, ge = (kh + 1) * ng / KS;       // its groups gb .. ge - 1
-  const int nck = CHUNKED ? (ge - gb + kChunkGroups - 1) / kChunkGroups : 1;
+  const int nck = CHUNKED ? (ge - gb + kCG - 1) / kCG : 1;
   const int ntiles = nck * NRB;
   const int row_bytes = K * IB / 8;
   const int h = lane >> 4, l16 = lane & 15;
@@ -223,40 +236,45 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
   const __amdgpu_buffer_rsrc_t rq = rsrc(A.q, (uint32_t)(A.batch * K));
   // the wave's groups of chunk c: g0 .. g0 + ngw - 1 (ngw <= PD)
   auto eighth = [&](int c, int &g0, int &ngw) {
-    const int base = gb + c * kChunkGroups;
-    const int ngc = ge - base < kChunkGroups ? ge - base : kChunkGroups;
+    const int base = gb + c * kCG;
+    const int ngc = ge - base < kCG ? ge - base : kCG;
     g0 = base + wave * ngc / kWaves;
     ngw = base + (wave + 1) * ngc / kWaves - g0;
   };
 
-  // codes of chunk c: lane (h, l16) takes token l16's codes 32 h .. 32 h + 31
-  // of each group of the eighth (tokens past the batch read as zeros; slots
-  // past the eighth repeat a group in range, their norm is taken as zero)
-  typedef u32x4v Raw[PD][2];
+  // codes of chunk c: lane (h, l16) takes token 16 th + l16's codes 32 h ..
+  // 32 h + 31 of each group of the eighth (tokens past the batch read as
+  // zeros; slots past the eighth repeat a group in range, their norm is taken
+  // as zero)
+  typedef u32x4v Raw[TH][PD][2];
   auto load_codes = [&](Raw &qraw, int c) {
     int g0, ngw;
     eighth(c, g0, ngw);
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int g = g0 + j < ng ? g0 + j : ng - 1;
-      const uint32_t off = (uint32_t)(l16 * K + g * kGroup + 32 * h);
-      qraw[j][0] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      qraw[j][1] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
-    }
+    for (int th = 0; th < TH; ++th)
+#pragma unroll
+      for (int j = 0; j < PD; ++j) {
+        const int g = g0 + j < ng ? g0 + j : ng - 1;
+        const uint32_t off = (uint32_t)((16 * th + l16) * K + g * kGroup + 32 * h);
+        qraw[th][j][0] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+        qraw[th][j][1] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+      }
   };
   // as fp16 A fragments: step s takes codes 8 s .. 8 s + 7
-  f16x8v a[PD][4];
+  f16x8v a[TH][PD][4];
   auto convert = [&](const Raw &qraw) {
 #pragma unroll
-    for (int j = 0; j < PD; ++j)
+    for (int th = 0; th < TH; ++th)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4v &v = qraw[j][s >> 1];
-        uint32_t o[4];
-        i8x4_f16((s & 1) ? v.z : v.x, o[0], o[1]);
-        i8x4_f16((s & 1) ? v.w : v.y, o[2], o[3]);
-        __builtin_memcpy(&a[j][s], o, 16);
-      }
+      for (int j = 0; j < PD; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4v &v = qraw[th][j][s >> 1];
+          uint32_t o[4];
+          i8x4_f16((s & 1) ? v.z : v.x, o[0], o[1]);
+          i8x4_f16((s & 1) ? v.w : v.y, o[2], o[3]);
+          __builtin_memcpy(&a[th][j][s], o, 16);
+        }
   };
 
   // a ring: tile tt's weight words of the lane and its row's norms (row l16
@@ -280,8 +298,8 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
   };
 
   const uint32_t lo = (uint32_t)(lane * entry_b<IB>()) & 255u;
-  // D[token][row] of tile tt: lane (h, l16) holds row l16, tokens 4 h + r;
-  // added into the row block's partial sums
+  // D[token][row] of tile tt: lane (h, l16) holds row l16, tokens
+  // 16 th + 4 h + r; added into the row block's partial sums
   auto consume = [&](const Ring &w, const NRing &n, int tt) {
     int g0, ngw;
     eighth(tt / NRB, g0, ngw);
@@ -293,22 +311,35 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
 #pragma unroll
     for (int m = 0; m < (PD + 1) / 2; ++m)
       nh[m] = m + 1 < NW ? __builtin_amdgcn_alignbit(n[m + 1], n[m], p * 16u) : n[m] >> (p * 16u);
-    f32x4v tot = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4v tot[TH];
+#pragma unroll
+    for (int th = 0; th < TH; ++th) tot[th] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
-      f32x4v acc = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4v acc[TH];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][s], levels_step<IB>(w[j], s, tab, lo), acc, 0, 0, 0);
+      for (int th = 0; th < TH; ++th) acc[th] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8v b = levels_step<IB>(w[j], s, tab, lo);
+#pragma unroll
+        for (int th = 0; th < TH; ++th)
+          acc[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[th][j][s], b, acc[th], 0, 0, 0);
+      }
       const float nv = j < ngw ? half_bits_to_float((uint16_t)(nh[j >> 1] >> ((j & 1) * 16))) : 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tot[r] = fmaf(nv, acc[r], tot[r]);
-    }
-    float *const slot = red + (wave * NRB + i) * 256 + lane;   // [r][lane]
+      for (int th = 0; th < TH; ++th)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (CHUNKED && tt >= NRB) tot[r] += slot[r * 64];
-      slot[r * 64] = tot[r];
+        for (int r = 0; r < 4; ++r) tot[th][r] = fmaf(nv, acc[th][r], tot[th][r]);
+    }
+#pragma unroll
+    for (int th = 0; th < TH; ++th) {
+      float *const slot = red + ((wave * NRB + i) * TH + th) * 256 + lane;   // [r][lane]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (CHUNKED && tt >= NRB) tot[th][r] += slot[r * 64];
+        slot[r * 64] = tot[th][r];
+      }
     }
   };
 
@@ -372,13 +403,14 @@ __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, Level
   __syncthreads();
   const float cfac = T.cscale * (1.0f / kGroup);
   constexpr int wrows = NRB * 16;              // the workgroup's rows, per token
-  for (int e = t; e < kTok * wrows; e += kThreadsV) {
+  for (int e = t; e < kTok * TH * wrows; e += kThreadsV) {
     const int tk = e / wrows, rr = e - tk * wrows;
     const int i = rr >> 4, row16 = rr & 15;
-    const int ln = 16 * (tk >> 2) + row16, r = tk & 3;
+    const int th = tk >> 4, t16 = tk & 15;
+    const int ln = 16 * (t16 >> 2) + row16, r = t16 & 3;
     float v = 0.0f;
 #pragma unroll
-    for (int w8 = 0; w8 < kWaves; ++w8) v += red[((w8 * NRB + i) * 4 + r) * 64 + ln];
+    for (int w8 = 0; w8 < kWaves; ++w8) v += red[(((w8 * NRB + i) * TH + th) * 4 + r) * 64 + ln];
     const int row = rg * wrows + rr;
     if (tk < A.batch && row < N) {
       if constexpr (KS == 1) A.y[(size_t)tk * N + row] = v * (A.scale[tk] * cfac);
@@ -398,14 +430,18 @@ bool cq_gemv_mma_supported(const bqm_cq_layout &L, int batch) {
   // 2 tokens only where K is one chunk: with chunks the VALU GEMV, which
   // holds no codes, is as fast for 2
   const int min_batch = L.cols <= kChunkGroups * kGroup ? 2 : 3;
-  return batch >= min_batch && batch <= kTok && L.cols % kGroup == 0 && L.cols <= kMaxCols &&
+  return batch >= min_batch && batch <= kMaxTok && L.cols % kGroup == 0 && L.cols <= kMaxCols &&
          (uint64_t)L.idx_bytes < (1u << 30) && (uint64_t)L.norms_count * 2 < (1u << 30);
 }
 
-hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
-                              const int8_t *q, const float *scale, int batch, float *y,
-                              int num_cus, hipStream_t s) {
-  // a workgroup per CU where that leaves each at most kRBMax row blocks, the
+namespace {
+
+template <int TH>
+hipError_t launch_mma_th(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                         const int8_t *q, const float *scale, int batch, float *y,
+                         int num_cus, hipStream_t s) {
+  constexpr int kCG = chunk_groups<TH>(), kRB = rb_max<TH>();
+  // a workgroup per CU where that leaves each at most kRB row blocks, the
   // count rounded up to a power of two
   const int rb_total = (L.rows + 15) / 16;
   const int per_cu = (rb_total + num_cus - 1) / num_cus;
@@ -414,8 +450,8 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
   // workgroup reads then outweigh its weights): split K in two (each
   // workgroup two row blocks, half the codes), the halves added into y after
   // a zero fill (the fill's launch costs as much as the split saves at 4 tokens)
-  const bool split = per_cu <= 1 && ng >= 2 * kChunkGroups && rb_total >= 2 && batch > 8;
-  const int nrb = split ? 2 : per_cu <= 1 ? 1 : per_cu <= 2 ? 2 : per_cu <= 4 ? 4 : kRBMax;
+  const bool split = per_cu <= 1 && ng >= 2 * kCG && rb_total >= 2 && batch > 8;
+  const int nrb = split ? 2 : per_cu <= 1 ? 1 : per_cu <= 2 ? 2 : per_cu <= 4 || kRB == 4 ? 4 : kRB;
   const int grid = (rb_total + nrb - 1) / nrb * (split ? 2 : 1);
   if (split) {
     const int n = batch * L.rows;
@@ -438,20 +474,21 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
     constexpr int IB = decltype(ib)::value, PD = decltype(pd)::value;
     constexpr bool CH = decltype(chunked)::value;
     if (CH && split) {
-      cq_gemv_mma_kernel<IB, PD, 2, CH, 2><<<grid, kThreadsV, 0, s>>>(A, T);
+      cq_gemv_mma_kernel<IB, PD, 2, CH, 2, TH><<<grid, kThreadsV, 0, s>>>(A, T);
       return hipGetLastError();
     }
     switch (nrb) {
-      case 1: cq_gemv_mma_kernel<IB, PD, 1, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 2: cq_gemv_mma_kernel<IB, PD, 2, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      case 4: cq_gemv_mma_kernel<IB, PD, 4, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
-      default: cq_gemv_mma_kernel<IB, PD, kRBMax, CH, 1><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 1: cq_gemv_mma_kernel<IB, PD, 1, CH, 1, TH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 2: cq_gemv_mma_kernel<IB, PD, 2, CH, 1, TH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      case 4: cq_gemv_mma_kernel<IB, PD, 4, CH, 1, TH><<<grid, kThreadsV, 0, s>>>(A, T); break;
+      default: cq_gemv_mma_kernel<IB, PD, kRB, CH, 1, TH><<<grid, kThreadsV, 0, s>>>(A, T); break;
     }
     return hipGetLastError();
   };
   auto go = [&](auto ib) -> hipError_t {
-    if (ng > kChunkGroups)
-      return with_nrb(ib, std::integral_constant<int, 4>{}, std::true_type{});
+    constexpr int kPDC = kCG / kWaves;             // groups of an eighth of a full chunk
+    if (ng > kCG)
+      return with_nrb(ib, std::integral_constant<int, kPDC>{}, std::true_type{});
     if (pd_need > 2) return with_nrb(ib, std::integral_constant<int, 4>{}, std::false_type{});
     if (pd_need > 1) return with_nrb(ib, std::integral_constant<int, 2>{}, std::false_type{});
     return with_nrb(ib, std::integral_constant<int, 1>{}, std::false_type{});
@@ -462,6 +499,15 @@ hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const
     case 3: return go(std::integral_constant<int, 3>{});
     default: return go(std::integral_constant<int, 4>{});
   }
+}
+
+}  // namespace
+
+hipError_t launch_cq_gemv_mma(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
+                              const int8_t *q, const float *scale, int batch, float *y,
+                              int num_cus, hipStream_t s) {
+  if (batch > kTok) return launch_mma_th<2>(blob, L, T, q, scale, batch, y, num_cus, s);
+  return launch_mma_th<1>(blob, L, T, q, scale, batch, y, num_cus, s);
 }
 
 }  // namespace bqm

@@ -284,12 +284,12 @@ def test_cq_gemm_every_tile(rows, cols, codebooks):
     P.check_cq(y, idx, n16, 128, 4, lv, q, s, P.TOL_FOLD, f"cq_gemm tile case m500 {rows}x{cols}")
 
 
-# Up to 32 tokens cq_gemm runs the decode kernels in launches of up to 16
-# tokens (exact fp16 products): those results meet the GEMV bar, which the
-# GEMM's one fp16 rounding a weight would not, and equal cq_gemv on each
-# 16-token slice bit for bit (17 tokens: a last launch of one token, the VALU
-# GEMV; 32: two matrix-core launches).  33 tokens take the GEMM (64 x 32
-# tiles for the 2- and 4-bit fields here: each group's steps in quarters).
+# Up to 32 tokens cq_gemm runs the batched decode kernel in one launch (two
+# 16-token halves on the same weight fragments; exact fp16 products): the
+# results meet the GEMV bar, which the GEMM's one fp16 rounding a weight would
+# not, and the first 16 tokens equal cq_gemv's 16-token launch bit for bit (the
+# same fragments and order).  33 tokens take the GEMM (64 x 32 tiles for the
+# 2- and 4-bit fields here: each group's steps in quarters).
 @pytest.mark.parametrize("code", [1, 2, 4, 5])
 @pytest.mark.parametrize("m", [17, 32, 33])
 def test_cq_gemm_few_tokens(code, m, codebooks):
@@ -302,10 +302,24 @@ def test_cq_gemm_few_tokens(code, m, codebooks):
     if m > 32:
         P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_FOLD, f"cq_gemm code {code} m{m} 300x1024 (GEMM)")
         return
-    P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"cq_gemm code {code} m{m} 300x1024 (decode kernels)")
-    for b0 in range(0, m, 16):
-        yb = host(B.cq_gemv(dev(blob), lay, cb, dev(q[b0:b0 + 16]), dev(s[b0:b0 + 16])))
-        assert np.array_equal(y[b0:b0 + 16], yb), f"tokens {b0}.."
+    P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"cq_gemm code {code} m{m} 300x1024 (decode kernel)")
+    yb = host(B.cq_gemv(dev(blob), lay, cb, dev(q[:16]), dev(s[:16])))
+    assert np.array_equal(y[:16], yb)
+
+
+# The two-half batched kernel on every shape class it meets: K in chunks of
+# 16 groups (4096, and 8320 = 65 groups: a ragged last chunk), 2 and 4 row
+# blocks a workgroup with ragged ends, and the K split in two workgroups
+# added into a zeroed y (16384 columns, one row block a CU); 24 tokens leave
+# 8 token columns of the second half empty.
+@pytest.mark.parametrize("rows,cols", [(300, 4096), (70, 8320), (5000, 2048), (9000, 512), (40, 16384)])
+@pytest.mark.parametrize("m", [24, 32])
+def test_cq_gemm_two_token_halves(rows, cols, m, codebooks):
+    rng = np.random.default_rng(1800 + rows + cols + m)
+    lv, idx, n16, blob, q, s = oracle_case(rng, rows, cols, 4, m, codebooks)
+    lay = B.cq_pack_info(rows, cols, 128, 4)
+    y = host(B.cq_gemm(dev(blob), lay, host_codebook(4, codebooks), dev(q), dev(s)))
+    P.check_cq(y, idx, n16, 128, 4, lv, q, s, P.TOL_F32, f"cq_gemm m{m} {rows}x{cols} (two token halves)")
 
 
 @pytest.mark.parametrize("rows,cols,batch", [(312, 312, 1), (104, 312, 1), (1092, 312, 1),
