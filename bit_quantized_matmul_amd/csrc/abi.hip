@@ -252,7 +252,7 @@ int cq_gemv(const void *blob, const bqm_cq_layout *layout, const float *codebook
   rc = make_table(layout->bits, codebook, &T);
   if (rc) return rc;
   const bool base3 = layout->bits == BQM_CQ_TERNARY_B3;
-  if (base3 ? !cq_gemv_t3_supported(*layout, batch) : (batch > 16 || !cq_gemv_supported(*layout, false)))
+  if (base3 ? !cq_gemv_t3_supported(*layout, batch) : (batch > 32 || !cq_gemv_supported(*layout, false)))
     return BQM_ENOTSUP;
   if (!aligned16(blob) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)y & 3u))
     return BQM_EALIGN;

@@ -39,7 +39,8 @@ enum {
   BQM_EINVAL = -1,  /* null pointer, bad shape, unknown bits code, bad codebook */
   BQM_EALIGN = -2,  /* a device pointer is not 16-byte aligned                 */
   BQM_ENOTSUP = -3, /* valid request the device path does not provide
-                       (group != 128, batch > 16, non-gfx950 device)           */
+                       (group != 128, a batch past the entry's limit,
+                       non-gfx950 device)                                      */
   BQM_EDEVICE = -4, /* HIP reported an error while launching                   */
   BQM_ERANGE = -5   /* reported through an encoder's status word, see cq_pack  */
 };
@@ -112,12 +113,13 @@ int act_fwht_quant_a8(const float *x, int m, int k, int group, int8_t *q, float 
  * (each finite and bfloat16-representable, hence exact in fp16 too;
  * BQM_EINVAL otherwise), NULL for bits 1, 5 and 6; q [device] int8 [batch, cols] from act_fwht_quant_a8;
  * scale [device] fp32 [batch]; y [device] fp32 [batch, rows].
- * 1 <= batch <= 16 and cols <= 36864 (one token's codes as fp16 fit in LDS
+ * 1 <= batch <= 32 and cols <= 36864 (one token's codes as fp16 fit in LDS
  * beside the level table; BQM_ENOTSUP past either).  group must be 128.  For batch >= 2
  * (>= 3 when cols > 4096) and cols <= 16384 the product runs on the matrix
  * cores in one pass over the weights for all tokens: exact fp16 levels x
  * exact fp16 codes, fp32 accumulation per group, fp32 norm per group, the
- * groups summed in a fixed order.  With more than 8 tokens, at most 16 rows
+ * groups summed in a fixed order (past 16 tokens as two 16-token halves on
+ * the same weight fragments).  With more than 8 tokens, at most 16 rows
  * a CU and at least 64 groups a row, the call is two launches: y is zeroed,
  * then two halves of K are summed as above and each half's scaled result is
  * added into y atomically (two addends onto zero: the same bits in either

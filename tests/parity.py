@@ -52,7 +52,7 @@ RECORDS: list[dict] = []
 def cq_gemv_tol(cols: int, batch: int) -> float:
     """Element tolerance of the cq_gemv / cq_gemv_f32 (with code buffers) route."""
     min_mma = 2 if cols <= MMA_ONE_CHUNK_COLS else 3
-    if min_mma <= batch <= 16 and cols <= MMA_MAX_COLS:
+    if min_mma <= batch <= 32 and cols <= MMA_MAX_COLS:
         return TOL_F32
     if batch > 4:
         return TOL_FOLD

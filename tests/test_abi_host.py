@@ -86,7 +86,7 @@ def test_device_entry_points_validate_before_touching_a_device(lib):
     assert lib.cq_gemv(p, ctypes.byref(bad), cb, p, p, 1, p, None) == E.BQM_EINVAL
     assert lib.cq_gemv(p, ctypes.byref(lay), None, p, p, 1, p, None) == E.BQM_EINVAL   # codebook needed
     assert lib.cq_gemv(p, ctypes.byref(lay), cb, p, p, 0, p, None) == E.BQM_EINVAL
-    assert lib.cq_gemv(p, ctypes.byref(lay), cb, p, p, 17, p, None) == E.BQM_ENOTSUP
+    assert lib.cq_gemv(p, ctypes.byref(lay), cb, p, p, 33, p, None) == E.BQM_ENOTSUP
     nonbf16 = (ctypes.c_float * 16)(*([0.1] * 16))     # 0.1 is not bfloat16-representable
     assert lib.cq_gemv(p, ctypes.byref(lay), nonbf16, p, p, 1, p, None) == E.BQM_EINVAL
     tern = binding.cq_pack_info(256, 512, 128, 5)

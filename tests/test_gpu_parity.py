@@ -165,6 +165,10 @@ def oracle_case(rng, rows, cols, code, batch, codebooks):
                                              (5000, 512, 6), (9000, 256, 16), (40000, 128, 7),
                                              (40, 5120, 8), (40, 5120, 3), (40, 5120, 2),
                                              (20, 20480, 5), (9, 36864, 8),
+                                             # 17..32 tokens: two 16-token halves (a
+                                             # ragged second half, 4 row blocks, K in
+                                             # chunks), past 16384 columns the GEMM
+                                             (300, 4096, 24), (9000, 512, 32), (20, 20480, 24),
                                              (300, 8192, 10), (33, 8320, 9), (1000, 12288, 16), (17, 16384, 12),
                                              (300, 8192, 6)])
 def test_cq_gemv_parity(code, rows, cols, batch, codebooks):
