@@ -14,8 +14,8 @@ The same line carries: ``roofline`` for the dominant kernel (the fused CQ GEMV
 on the 4096x14336 down-projection shape: mean launch duration over a HIP graph
 of back-to-back HBM-cold launches, timed with HIP events on the launch stream), the prefill GEMM (512 tokens, TFLOP/s), the Minueza-shaped
 Q4_0 decode pass and the same pass as a 512-token prefill (q4_0_gemm), the
-bit-width sweep, the same decode layer shapes at 4 and
-16 tokens per call (``batched_decode_cb4``), and ``cpu_baseline``: the CPU
+bit-width sweep, the same decode layer shapes at 4, 16
+and 32 tokens per call (``batched_decode_cb4``), and ``cpu_baseline``: the CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -746,11 +746,15 @@ def bench_sweep(B, torch, dev, cbs, steps):
     return out
 
 
-def bench_batched(B, torch, dev, cbs, steps, batches=(4, 16)):
+def bench_batched(B, torch, dev, cbs, steps, batches=(4, 16, 32)):
     """Several decode tokens at once on the 8B layer shapes (cb4): one cq_gemv per
-    matrix, whose one pass over the weights on the matrix cores serves every token."""
+    matrix, whose one pass over the weights on the matrix cores serves every token
+    (32 tokens: two 16-token halves on the same weight fragments; their
+    activations come from a stream of their own, so the 4- and 16-token inputs
+    stay as they were)."""
     from bit_quantized_matmul_amd import inputs
     rng = inputs.rng_for(11)
+    rng32 = inputs.rng_for(12)
     out = {}
     for (rows, cols) in inputs.DECODE_8B_SHAPES:
         w = torch.from_numpy(inputs.weight_matrix(rng, rows, cols, outliers=True)).to(dev)
@@ -761,7 +765,7 @@ def bench_batched(B, torch, dev, cbs, steps, batches=(4, 16)):
         n = pool_copies(nb)
         pool = [blob] + [blob.clone() for _ in range(n - 1)]
         for batch in batches:
-            x = torch.from_numpy(inputs.activations(rng, batch, cols)).to(dev)
+            x = torch.from_numpy(inputs.activations(rng if batch <= 16 else rng32, batch, cols)).to(dev)
             q, s = B.act_fwht_quant_a8(x)
             y = torch.empty((batch, rows), dtype=torch.float32, device=dev)
             d = graph_mean_ms(torch, [
@@ -969,7 +973,7 @@ def main():
     log("sweep done")
     bat = bench_batched(B, torch, dev, cbs, args.steps)
     log(f"batched decode step: 4 tokens {bat['step_b4']['us']:.1f} us, "
-        f"16 tokens {bat['step_b16']['us']:.1f} us")
+        f"16 tokens {bat['step_b16']['us']:.1f} us, 32 tokens {bat['step_b32']['us']:.1f} us")
     floor = bench_read_floor(torch, dev)
     log(f"30 MB vendor reads: row sums {floor['row_sums']['us']:.2f} us, fp32 mv {floor['fp32_gemv_torch_mv']['us']:.2f} us, "
         f"empty launch {floor['empty_launch_us']:.2f} us")

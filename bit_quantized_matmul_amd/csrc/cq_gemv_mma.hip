@@ -41,7 +41,9 @@ constexpr int kMaxTok = 2 * kTok;       // tokens a launch takes (two 16-token h
 constexpr int kRBMax = 8;               // row blocks a workgroup finishes
 constexpr int kChunkGroups = 32;        // K chunk: the groups whose codes the waves hold at once
 // With two token halves (TH = 2) a wave holds twice the A fragments and
-// partial sums: the K chunk and the row blocks a workgroup takes are halved.
+// partial sums: past one chunk of 32 groups (where the next chunk's codes are
+// in flight too) the K chunk is halved, and so are the row blocks a workgroup
+// takes.
 template <int TH> constexpr int chunk_groups() { return kChunkGroups / TH; }
 template <int TH> constexpr int rb_max() { return kRBMax / TH; }
 constexpr int kMaxCols = 16384;         // as the fused GEMV's limit
@@ -215,7 +217,7 @@ struct MmaArgs {
 // (1: up to 16 tokens; 2: up to 32, each B fragment feeding one MFMA per half).
 template <int IB, int PD, int NRB, bool CHUNKED, int KS, int TH>
 __global__ __launch_bounds__(kThreadsV) void cq_gemv_mma_kernel(MmaArgs A, LevelTable T) {
-  constexpr int kCG = chunk_groups<TH>();
+  constexpr int kCG = CHUNKED ? chunk_groups<TH>() : kChunkGroups;
   // one array, the table at its start: table addresses need no base added
   __shared__ __align__(16) uint8_t lds[kTabBytes + red_bytes<NRB, TH>()];
   uint8_t *const tab = lds;
@@ -440,7 +442,7 @@ template <int TH>
 hipError_t launch_mma_th(const uint8_t *blob, const bqm_cq_layout &L, const LevelTable &T,
                          const int8_t *q, const float *scale, int batch, float *y,
                          int num_cus, hipStream_t s) {
-  constexpr int kCG = chunk_groups<TH>(), kRB = rb_max<TH>();
+  constexpr int kCG = chunk_groups<TH>(), kRB = rb_max<TH>();   // (kCG: when chunked)
   // a workgroup per CU where that leaves each at most kRB row blocks, the
   // count rounded up to a power of two
   const int rb_total = (L.rows + 15) / 16;
@@ -450,7 +452,7 @@ hipError_t launch_mma_th(const uint8_t *blob, const bqm_cq_layout &L, const Leve
   // workgroup reads then outweigh its weights): split K in two (each
   // workgroup two row blocks, half the codes), the halves added into y after
   // a zero fill (the fill's launch costs as much as the split saves at 4 tokens)
-  const bool split = per_cu <= 1 && ng >= 2 * kCG && rb_total >= 2 && batch > 8;
+  const bool split = per_cu <= 1 && ng >= 2 * kChunkGroups && rb_total >= 2 && batch > 8;
   const int nrb = split ? 2 : per_cu <= 1 ? 1 : per_cu <= 2 ? 2 : per_cu <= 4 || kRB == 4 ? 4 : kRB;
   const int grid = (rb_total + nrb - 1) / nrb * (split ? 2 : 1);
   if (split) {
@@ -487,7 +489,7 @@ hipError_t launch_mma_th(const uint8_t *blob, const bqm_cq_layout &L, const Leve
   };
   auto go = [&](auto ib) -> hipError_t {
     constexpr int kPDC = kCG / kWaves;             // groups of an eighth of a full chunk
-    if (ng > kCG)
+    if (ng > kChunkGroups)
       return with_nrb(ib, std::integral_constant<int, kPDC>{}, std::true_type{});
     if (pd_need > 2) return with_nrb(ib, std::integral_constant<int, 4>{}, std::false_type{});
     if (pd_need > 1) return with_nrb(ib, std::integral_constant<int, 2>{}, std::false_type{});
