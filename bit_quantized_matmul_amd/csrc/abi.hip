@@ -372,7 +372,7 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
                                        (hipStream_t)stream));
   // up to 32 tokens: the batched decode kernel reads the weights once for all
   // of them and beats the GEMM's few tiles (measured at 32 tokens: 4096x4096
-  // 10.8 against 19.0 us, 14336x4096 15.9 against 24.1, 4096x14336 21.0
+  // 8.5 against 19.0 us, 14336x4096 15.2 against 24.1, 4096x14336 21.8
   // against 54.8; at 64 tokens, in two launches, the GEMM wins on three of
   // the four shapes)
   if (m <= kGemvTokensForGemm && cq_gemv_mma_supported(*layout, 16))
