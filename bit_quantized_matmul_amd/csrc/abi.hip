@@ -375,8 +375,21 @@ int cq_gemm(const void *blob, const bqm_cq_layout *layout, const float *codebook
   // 8.5 against 19.0 us, 14336x4096 15.2 against 24.1, 4096x14336 21.8
   // against 54.8; at 64 tokens, in two launches, the GEMM wins on three of
   // the four shapes)
-  if (m <= kGemvTokensForGemm && cq_gemv_mma_supported(*layout, 16))
-    return status_of(launch_cq_gemv((const uint8_t *)blob, *layout, T, q, scale, m, y, cus, (hipStream_t)stream));
+  // Up to 64 tokens, where even 64 x 64 GEMM tiles would leave CUs idle, the
+  // same in launches of 32 (at 64 tokens: 4096x4096 17.0 against 19.2 us,
+  // 4096x14336 43.6 against 54.4; 14336x4096 fills the CUs with 64 x 64 tiles
+  // and keeps the GEMM, 24.8 against 30.4)
+  const int64_t t64 = (int64_t)((m + 63) / 64) * ((layout->rows + 63) / 64);
+  const bool few = m <= kGemvTokensForGemm || (m <= 2 * kGemvTokensForGemm && t64 < (int64_t)cus * 7 / 8);
+  if (few && cq_gemv_mma_supported(*layout, 16)) {
+    for (int b0 = 0; b0 < m; b0 += kGemvTokensForGemm) {
+      const int nb = m - b0 < kGemvTokensForGemm ? m - b0 : kGemvTokensForGemm;
+      const hipError_t e = launch_cq_gemv((const uint8_t *)blob, *layout, T, q + (size_t)b0 * layout->cols,
+                                          scale + b0, nb, y + (size_t)b0 * layout->rows, cus, (hipStream_t)stream);
+      if (e != hipSuccess) return BQM_EDEVICE;
+    }
+    return BQM_OK;
+  }
   return status_of(launch_cq_gemm((const uint8_t *)blob, *layout, T, q, scale, m, y, cus,
                                   (hipStream_t)stream));
 }

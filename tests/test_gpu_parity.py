@@ -289,13 +289,14 @@ def test_cq_gemm_every_tile(rows, cols, codebooks):
 
 
 # Up to 32 tokens cq_gemm runs the batched decode kernel in one launch (two
-# 16-token halves on the same weight fragments; exact fp16 products): the
+# 16-token halves on the same weight fragments; exact fp16 products), up to 64
+# in launches of 32 where the GEMM's tiles would leave CUs idle (as here): the
 # results meet the GEMV bar, which the GEMM's one fp16 rounding a weight would
 # not, and the first 16 tokens equal cq_gemv's 16-token launch bit for bit (the
-# same fragments and order).  33 tokens take the GEMM (64 x 32 tiles for the
+# same fragments and order).  65 tokens take the GEMM (64 x 32 tiles for the
 # 2- and 4-bit fields here: each group's steps in quarters).
 @pytest.mark.parametrize("code", [1, 2, 4, 5])
-@pytest.mark.parametrize("m", [17, 32, 33])
+@pytest.mark.parametrize("m", [17, 32, 48, 65])
 def test_cq_gemm_few_tokens(code, m, codebooks):
     rng = np.random.default_rng(1700 + code + m)
     rows, cols = 300, 1024
@@ -303,7 +304,7 @@ def test_cq_gemm_few_tokens(code, m, codebooks):
     lay = B.cq_pack_info(rows, cols, 128, code)
     cb = host_codebook(code, codebooks)
     y = host(B.cq_gemm(dev(blob), lay, cb, dev(q), dev(s)))
-    if m > 32:
+    if m > 64:
         P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_FOLD, f"cq_gemm code {code} m{m} 300x1024 (GEMM)")
         return
     P.check_cq(y, idx, n16, 128, code, lv, q, s, P.TOL_F32, f"cq_gemm code {code} m{m} 300x1024 (decode kernel)")
