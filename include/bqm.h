@@ -211,9 +211,10 @@ int cq_gemv_f32_noalloc(const void *blob, const bqm_cq_layout *layout, const flo
  * exact fp16 integers; the matrix cores accumulate in fp32 and the token
  * scale is applied in fp32.  m >= 1, group must be 128.
  * Up to 32 tokens (cols <= 16384, bits 1-5) the call runs the batched
- * decode kernel of cq_gemv instead, one launch for all tokens: its products
- * are exact (no fp16 rounding of level x norm), so the bound above holds with
- * room.
+ * decode kernel of cq_gemv instead, one launch for all tokens, and up to 64
+ * tokens in launches of 32 when fewer than 7/8 of the CUs would get a 64 x 64
+ * tile: its products are exact (no fp16 rounding of level x norm), so the
+ * bound above holds with room.
  * Base-3 ternary (bits 6): exact int32 group sums of digit minus one times
  * code on the int8 matrix cores, each scaled by the group's fp32 norm and
  * added in fp32 in group order; m <= 16 tokens (with cols <= 16384) run the
